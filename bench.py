@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark: InstanceNorm2d fp32 on x[112,64,512,512] (7168 slices x 262144), one MI355X.
+
+A step is one inorm_forward call over the whole tensor (statistics + normalize, inputs already
+in HBM). The metric is effective bandwidth = minimum algorithmic bytes / time, with
+min bytes = 4*N*C*H*W read + 4*N*C*H*W written = 15,032,385,536 B, against the 8 TB/s HBM peak.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value / ms_per_step  from HIP events around the K timed steps on the launch stream;
+  roofline             the dominant kernel's achieved GB/s = algorithmic bytes per launch /
+                       its average launch duration (events around each launch), vs 8000 GB/s;
+                       traffic = HBM bytes per launch from the committed rocprofv3 counter
+                       summary when it was taken on the current kernel source, else null;
+  cpu_baseline         the fp64 oracle timed on a bounded sample of the same slices on the
+                       host cores (rank 0, one GPU), with the sample's max |gpu - oracle|;
+  extra                the plain streaming-copy ceiling on the same bytes and the other
+                       workloads' times (skipped with --no-extra).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+N, C, H, W = 112, 64, 512, 512
+S = H * W
+MIN_BYTES = 2 * 4 * N * C * S
+METRIC = "InstanceNorm2d fp32 effective GB/s (min bytes/time) and % of HBM peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "inorm_resident_112x64x512x512_traffic.json")
+KERNEL_SOURCES = ["normalization_reductions_amd/csrc/inorm_resident.hip",
+                  "normalization_reductions_amd/csrc/common.hpp",
+                  "normalization_reductions_amd/csrc/internal.hpp"]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, "no committed counter summary"
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel source changed since the counters were taken"
+    return t.get("hbm_bytes_per_launch"), "from %s" % os.path.relpath(TRAFFIC_FILE, ROOT)
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Returns (total ms for `steps` calls, mean ms per call measured around each call)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0.record()
+    for k in range(steps):
+        starts[k].record()
+        fn()
+        ends[k].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return total, sum(per) / len(per), sorted(per)[len(per) // 2]
+
+
+def cpu_baseline(x, y, budget_s, torch):
+    """fp64 oracle on the first M slices, M sized to ~budget_s of CPU time."""
+    import numpy as np
+
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    xv = x.view(N * C, S)
+    yv = y.view(N * C, S)
+    m0 = 16
+    xs = xv[:m0].cpu().numpy()
+    t = time.perf_counter()
+    oracle.instance_norm_slices(xs, nthreads=threads)
+    t_cal = max(time.perf_counter() - t, 1e-3)
+    m = int(min(N * C, max(m0, m0 * budget_s / t_cal)))
+    m = max(threads, m // threads * threads)
+    xs = xv[:m].cpu().numpy()
+    t = time.perf_counter()
+    ref = oracle.instance_norm_slices(xs, nthreads=threads)
+    dt = time.perf_counter() - t
+    ys = yv[:m].cpu().numpy()
+    err = float(np.max(np.abs(ys.astype(np.float64) - ref)))
+    gbps = (2 * 4 * m * S) / dt / 1e9
+    log("cpu oracle: %d slices in %.2f s on %d threads -> %.3f GB/s; sample max_abs_err %.3e"
+        % (m, dt, threads, gbps, err))
+    return ({"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+             "sample": "first %d of %d slices (%d x 262144 fp32), fp64 oracle, %.1f s wall"
+                       % (m, N * C, m, dt)},
+            {"slices": m, "max_abs_err": err})
+
+
+def extras(torch, nra, x, y, steps, warmup):
+    import numpy as np
+
+    import synth
+
+    out = {}
+    # streaming copy of the same bytes: the practical HBM ceiling
+    tot, per, med = time_calls(lambda: nra.stream_copy(x, y), steps, warmup, torch)
+    out["copy_ceiling_GBps"] = round(MIN_BYTES / (per / 1e3) / 1e9, 1)
+    log("stream copy of the same bytes: %.3f ms -> %.1f GB/s" % (per, out["copy_ceiling_GBps"]))
+    # the same workload through the two-pass streaming variant
+    tot, per, med = time_calls(lambda: nra.inorm_forward(x, y, variant=nra.NR_VARIANT_SPLIT),
+                               steps, warmup, torch)
+    out["split_variant_GBps"] = round(MIN_BYTES / (per / 1e3) / 1e9, 1)
+    log("split (2R+1W) variant: %.3f ms -> %.1f GB/s effective" % (per, out["split_variant_GBps"]))
+
+    dev = x.device
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    i2 = synth.host_inputs(2)
+    x2 = T(i2["x"])
+    y2 = torch.empty_like(x2)
+    tot, per, med = time_calls(lambda: nra.inorm_forward(x2, y2), steps, warmup, torch)
+    b2 = 2 * 4 * x2.numel()
+    out["inorm_16x64x256x256"] = {"ms": round(per, 4), "GBps": round(b2 / (per / 1e3) / 1e9, 1)}
+    log("inorm x[16,64,256,256]: %.4f ms -> %.1f GB/s" % (per, b2 / (per / 1e3) / 1e9))
+    del x2, y2
+
+    i4 = synth.host_inputs(4)
+    a4 = (T(i4["x"]), T(i4["w"]), T(i4["b"]))
+    g4, be4 = T(i4["gamma"]), T(i4["beta"])
+    o4 = torch.empty((128, 64, 62, 62), device=dev)
+    f4 = lambda: nra.conv_norm_epilogue_forward(*a4, out=o4, norm=nra.NR_NORM_BATCH_TRAIN,
+                                                gamma=g4, beta=be4, out_scale=2.0)
+    tot, per, med = time_calls(f4, steps, warmup, torch)
+    out["conv2d_bn_train_x2_128x8x64x64"] = {"ms": round(per, 4),
+                                             "conv_TFLOPs": round(2 * 128 * 64 * 62 * 62 * 72 / (per / 1e3) / 1e12, 2)}
+    log("conv2d+bn_train+x2: %.4f ms" % per)
+
+    i5 = synth.host_inputs(5)
+    a5 = (T(i5["x"]), T(i5["w"]), T(i5["b"]))
+    m5 = T(i5["mult"])
+    o5 = torch.empty((128, 14, 30, 30), device=dev)
+    f5 = lambda: nra.conv_norm_epilogue_forward(*a5, out=o5, norm=nra.NR_NORM_INSTANCE,
+                                                pre_mul=m5, clamp=(-1.0, 1.0), post_mul=m5,
+                                                reduce_max_c=True)
+    tot, per, med = time_calls(f5, steps, warmup, torch)
+    out["conv3d_in3d_clamp_maxc_128x3x16x32x32"] = {
+        "ms": round(per, 4), "conv_TFLOPs": round(2 * 128 * 16 * 12600 * 81 / (per / 1e3) / 1e12, 2)}
+    log("conv3d+IN3d+clamp+max_c: %.4f ms" % per)
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--variant", choices=["auto", "resident", "split"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: instance norm shards over the batch with no "
+              "communication, and no multi-GPU path is built (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import normalization_reductions_amd as nra
+    import synth
+
+    dev = torch.device("cuda:0")
+    variant = {"auto": nra.NR_VARIANT_AUTO, "resident": nra.NR_VARIANT_RESIDENT,
+               "split": nra.NR_VARIANT_SPLIT}[args.variant]
+    log("%s; drawing x[%d,%d,%d,%d] on the device" % (nra.version(), N, C, H, W))
+    x = synth.device_inputs_cfg3(dev)["x"]
+    y = torch.empty_like(x)
+    ws = torch.zeros(nra.inorm_workspace_size(N, C, S), dtype=torch.uint8, device=dev)
+
+    step = lambda: nra.inorm_forward(x, y, eps=1e-5, workspace=ws, variant=variant)
+    total_ms, launch_ms, launch_med = time_calls(step, args.steps, args.warmup, torch)
+    flags = nra.workspace_check(ws)
+    if flags:
+        log("workspace flags %#x: a co-resident wait gave up; results invalid" % flags)
+        return 1
+    ms = total_ms / args.steps
+    value = MIN_BYTES / (ms / 1e3) / 1e9
+    achieved = MIN_BYTES / (launch_ms / 1e3) / 1e9
+    log("%d steps: %.4f ms/step -> %.1f GB/s (%.1f%% of %.0f GB/s); per launch %.4f ms (median %.4f)"
+        % (args.steps, ms, value, 100 * value / HBM_PEAK_GBPS, HBM_PEAK_GBPS, launch_ms, launch_med))
+    traffic, tnote = committed_traffic()
+    log("traffic: %s (%s)" % (traffic, tnote))
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: x ~ N(0,1) drawn on the device with a seeded generator",
+        "config": {"workload": "InstanceNorm2d x[112,64,512,512] fp32, eps=1e-5, affine=False",
+                   "N": N, "C": C, "H": H, "W": W, "min_bytes_per_step": MIN_BYTES,
+                   "variant": args.variant},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "inorm_resident_kernel<512,16> (read-once, 8 parts/slice)"
+                               if args.variant != "split" else "split partial/merge/apply"},
+        "cpu_baseline": None,
+    }
+    if not args.no_extra:
+        res["extra"] = extras(torch, nra, x, y, args.steps, min(args.warmup, 3))
+        step()  # y again holds the instance norm of x for the baseline comparison
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        cb, par = cpu_baseline(x, y, args.cpu_seconds, torch)
+        res["cpu_baseline"] = cb
+        res["parity_sample"] = par
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,190 @@
+/*
+ * normred.h -- C ABI of the per-slice normalization library (libnormred.so), MI355X / gfx950.
+ *
+ * Three operations, as the source pages state them (pages of the "POPCORNBENCH / Kimi-K2.6"
+ * kernel-task traces):
+ *   IN2d page -- task l1_p34: InstanceNorm2d on x[112,64,512,512];
+ *   BN page   -- task l2_p73: Conv2d(8->64,k=3) -> BatchNorm2d(64) -> x2.0;
+ *   IN3d page -- task l2_p79: Conv3d(3->16,k=3) -> xmultiplier -> InstanceNorm3d -> clamp ->
+ *                xmultiplier -> max over channels.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major fp32 in DEVICE memory. The caller allocates and owns every
+ *     buffer (inputs, outputs, workspace); the library never allocates, frees or synchronizes
+ *     inside these calls.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns at once.
+ *   - Arguments are validated on the host before anything is enqueued; a rejected call returns
+ *     a non-zero nr_status, enqueues nothing and leaves every buffer untouched. The message for
+ *     the most recent failure on the calling thread is nr_last_error().
+ *   - NR_ERR_HIP reports a HIP runtime error raised while enqueueing. Faults inside kernels
+ *     surface at the caller's next synchronization, as with any HIP launch.
+ *   - Results are deterministic: the same inputs and shapes give bit-identical outputs on
+ *     every run (fixed reduction order; no floating-point atomics).
+ *   - Workspace: a device buffer of at least the size the matching *_workspace_size query
+ *     returns. It must be zero-filled once before its first use (nr_workspace_clear, or
+ *     hipMemset); every call leaves it valid for the next call. Calls that share a workspace
+ *     must be ordered (same stream, or synchronized): concurrent calls on one workspace race.
+ */
+#ifndef NORMRED_H
+#define NORMRED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nr_status {
+    NR_OK = 0,
+    NR_ERR_INVALID_ARG = 1, /* null pointer, non-positive or overflowing size, bad option */
+    NR_ERR_MISALIGNED = 2,  /* a pointer misaligned for its element type (4 bytes for fp32) */
+    NR_ERR_UNSUPPORTED = 3, /* a valid request this library does not implement (e.g. ksize != 3) */
+    NR_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query */
+    NR_ERR_HIP = 5          /* HIP runtime error while enqueueing */
+} nr_status;
+
+/* Message for the last non-OK status returned on this thread ("" if none). Never NULL. */
+const char* nr_last_error(void);
+
+/* Library version string, e.g. "normred 0.1.0 gfx950". */
+const char* nr_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Instance normalization.
+ *
+ * IN2d page, statement of the op (and IN3d page, its InstanceNorm3d reading): for every
+ * (n, c) slice of S = H*W (or D*H*W) elements, mean and BIASED variance over the slice, then
+ *     y = (x - mean) / sqrt(var + eps)              (affine = False, the pages' default)
+ * and, when gamma/beta are given, y = that * gamma[c] + beta[c].
+ *
+ * x, y       : [N, C, S] fp32 device buffers. y may equal x (in place); partial overlap is
+ *              rejected (NR_ERR_INVALID_ARG).
+ * N, C, S    : sizes; S >= 1, N >= 0, C >= 0. N*C == 0 is an empty batch: NR_OK, nothing
+ *              enqueued (workspace may then be NULL). N*C*S*4 must fit in int64.
+ * eps        : added to the variance inside the square root (the pages use 1e-5); >= 0.
+ * gamma,beta : [C] device buffers, or both NULL (affine = False). One without the other is
+ *              rejected.
+ * save_mean, save_invstd : [N*C] device outputs, or NULL: the slice mean and 1/sqrt(var+eps).
+ * workspace  : device buffer of >= inorm_workspace_size(N, C, S) bytes (see conventions).
+ * ------------------------------------------------------------------------------------------ */
+size_t inorm_workspace_size(int64_t N, int64_t C, int64_t S);
+
+nr_status inorm_forward(const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps,
+                        const float* gamma, const float* beta, float* save_mean,
+                        float* save_invstd, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Kernel variants for inorm_forward_ex (benchmarks and tests; inorm_forward = AUTO). */
+#define NR_VARIANT_AUTO 0     /* the library's choice for the shape */
+#define NR_VARIANT_RESIDENT 1 /* read-once: each slice held in registers, split over 1..16
+                                 co-resident workgroups that exchange partial statistics */
+#define NR_VARIANT_SPLIT 2    /* streaming two-pass: partial statistics per chunk, a fixed-order
+                                 merge, then a normalize pass (reads x twice) */
+
+/* As inorm_forward, with an explicit variant. A variant that cannot run this shape (e.g.
+ * RESIDENT with a slice beyond 16 parts, or unaligned data) returns NR_ERR_UNSUPPORTED. */
+nr_status inorm_forward_ex(const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps,
+                           const float* gamma, const float* beta, float* save_mean,
+                           float* save_invstd, void* workspace, size_t workspace_bytes,
+                           int variant, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Training-mode batch normalization, then a scale.
+ *
+ * BN page, opening analysis: in training mode the output uses the batch statistics -- per
+ * channel c, mean and BIASED variance over all (n, spatial) -- and
+ *     y = ((x - mean_c) / sqrt(var_c + eps) * gamma[c] + beta[c]) * out_scale
+ * (the page's model multiplies by scaling_factor = 2.0 after the norm). Running statistics
+ * are neither read nor written.
+ *
+ * x, y       : [N, C, S] fp32 device buffers; y may equal x.
+ * N, C, S    : N >= 1 and S >= 1 (statistics over nothing are undefined); C >= 0 (C == 0 is
+ *              a no-op).
+ * gamma,beta : [C] device buffers, or both NULL (identity affine).
+ * out_scale  : final multiplier (1.0f for plain batch norm).
+ * save_mean, save_invstd : [C] device outputs, or NULL.
+ * workspace  : >= bn_train_workspace_size(N, C, S) bytes.
+ * ------------------------------------------------------------------------------------------ */
+size_t bn_train_workspace_size(int64_t N, int64_t C, int64_t S);
+
+nr_status bn_train_forward(const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps,
+                           const float* gamma, const float* beta, float out_scale,
+                           float* save_mean, float* save_invstd, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Convolution (k = 3, stride 1, no padding, with bias) -> normalization -> epilogue.
+ *
+ * The step order covers both model pages:
+ *   c  = conv(x, w) + b        cross-correlation, no kernel flip (BN page, its direct-conv
+ *                              indexing; IN3d page: output extent = input extent - 2)
+ *   s  = c * pre_mul[k]        (IN3d page: first multiply by the [C,1,1,1] multiplier)
+ *   z  = (s - mean) / sqrt(var + eps)
+ *        NR_NORM_BATCH_TRAIN: statistics per channel k over (n, spatial)   (BN page)
+ *        NR_NORM_INSTANCE   : statistics per (n, k) over spatial           (IN3d page)
+ *   z  = z * gamma[k] + beta[k]  (BN page: affine batch norm)
+ *   z  = z * out_scale           (BN page: x scaling_factor)
+ *   z  = min(max(z, lo), hi)     (IN3d page: clamp, in its min(max()) order), if clamp
+ *   u  = z * post_mul[k]         (IN3d page: second multiply)
+ *   out = max over k of u        if reduce_max_c (IN3d page: max over dim 1, values only)
+ *       = u                      otherwise
+ *
+ * Shapes: x [N, C_in, (D,) H, W]; w [C_out, C_in, (3,) 3, 3]; b [C_out] or NULL;
+ * out [N, (D-2,) H-2, W-2] if reduce_max_c else [N, C_out, (D-2,) H-2, W-2].
+ * spatial_dims is 2 (D ignored) or 3. Every optional [C_out] pointer may be NULL. N == 0 is an
+ * empty batch (NR_OK, nothing enqueued).
+ * ------------------------------------------------------------------------------------------ */
+#define NR_NORM_BATCH_TRAIN 1
+#define NR_NORM_INSTANCE 2
+
+typedef struct nr_conv_norm_desc {
+    int32_t spatial_dims;        /* 2 or 3 */
+    int32_t ksize;               /* must be 3, else NR_ERR_UNSUPPORTED */
+    int64_t N, C_in, C_out;      /* >= 1 each */
+    int64_t in_d, in_h, in_w;    /* input extent; in_d ignored when spatial_dims == 2; >= 3 */
+    int32_t norm;                /* NR_NORM_BATCH_TRAIN or NR_NORM_INSTANCE */
+    float eps;                   /* >= 0 */
+    const float* pre_mul;        /* [C_out] or NULL */
+    const float* gamma;          /* [C_out] or NULL */
+    const float* beta;           /* [C_out] or NULL */
+    float out_scale;             /* 1.0f = none */
+    int32_t clamp;               /* 0 or 1 */
+    float clamp_lo, clamp_hi;    /* used when clamp = 1; lo <= hi */
+    const float* post_mul;       /* [C_out] or NULL */
+    int32_t reduce_max_c;        /* 0 or 1 */
+} nr_conv_norm_desc;
+
+/* 0 if the descriptor is invalid. */
+size_t conv_norm_epilogue_workspace_size(const nr_conv_norm_desc* d);
+
+nr_status conv_norm_epilogue_forward(const nr_conv_norm_desc* d, const float* x, const float* w,
+                                     const float* b, float* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Workspace and measurement helpers.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Zero-fill `bytes` of a workspace on `stream` with a fill kernel (no hipMemset, so it is
+ * also safe inside a captured graph). */
+nr_status nr_workspace_clear(void* workspace, size_t bytes, hipStream_t stream);
+
+/* Reads the workspace's sticky error word (synchronizes `stream` first). *flags_out = 0 when
+ * every co-resident exchange completed; bit 0 = a bounded wait gave up (results of that call
+ * are invalid). Clears the word afterwards. */
+nr_status nr_workspace_check(void* workspace, size_t bytes, hipStream_t stream, uint32_t* flags_out);
+
+/* Plain streaming copy dst[i] = src[i], i < n, with 16-byte loads/stores: the HBM ceiling the
+ * normalization kernels are compared against, and the calibration kernel for byte counters.
+ * src/dst 16-byte aligned and n % 4 == 0 for the vector path; anything else takes a scalar
+ * path. */
+nr_status nr_stream_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMRED_H */

@@ -1,0 +1,528 @@
+// abi.cpp -- the extern "C" boundary of libnormred: argument validation, variant planning,
+// workspace layout and kernel dispatch. Validation never touches the HIP runtime, so every
+// rejection path works (and is tested) on machines without a GPU.
+#include "normred.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.hpp"
+
+using namespace nr;
+
+namespace {
+
+thread_local std::string t_err;
+
+nr_status fail(nr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+nr_status fail(nr_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return s;
+}
+
+nr_status hip_fail(hipError_t e, const char* where)
+{
+    return fail(NR_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Total element count N*C*S (and its byte size) without overflow. N and C may be 0 when
+// allow_empty (an empty batch is a no-op); S must be >= 1 (a statistic over nothing is undefined).
+nr_status check_sizes(int64_t N, int64_t C, int64_t S, int64_t* total, const char* fn,
+                      bool allow_empty = true)
+{
+    const int64_t lo = allow_empty ? 0 : 1;
+    if (N < lo || C < lo || S < 1)
+        return fail(NR_ERR_INVALID_ARG, "%s: sizes out of range (N=%lld C=%lld S=%lld)", fn,
+                    (long long)N, (long long)C, (long long)S);
+    int64_t nc = 0, t = 0, bytes = 0;
+    if (!mul_ok(N, C, &nc) || !mul_ok(nc, S, &t) || !mul_ok(t, 4, &bytes))
+        return fail(NR_ERR_INVALID_ARG, "%s: N*C*S overflows", fn);
+    *total = t;
+    return NR_OK;
+}
+
+nr_status check_eps(float eps, const char* fn)
+{
+    if (!std::isfinite(eps) || eps < 0.f) return fail(NR_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    return NR_OK;
+}
+
+// Optional per-channel fp32 vector: NULL or 4-byte aligned.
+nr_status check_opt(const void* p, const char* name, const char* fn)
+{
+    if (p && !aligned(p, 4)) return fail(NR_ERR_MISALIGNED, "%s: %s is not 4-byte aligned", fn, name);
+    return NR_OK;
+}
+
+bool ranges_partially_overlap(const float* a, const float* b, int64_t n)
+{
+    if (a == b) return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t len = (uintptr_t)n * 4u;
+    return pa < pb + len && pb < pa + len;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Instance-norm planning.
+// ---------------------------------------------------------------------------------------------
+// Optional override of the resident configuration, "block,vec" (tuning, tests and benchmarks
+// only; read on every call).
+bool resident_override(int* block, int* vec)
+{
+    const char* e = getenv("NORMRED_RESIDENT_CFG");
+    int b = 0, v = 0;
+    if (e && sscanf(e, "%d,%d", &b, &v) == 2 && b > 0 && v > 0) {
+        *block = b;
+        *vec = v;
+        return true;
+    }
+    return false;
+}
+
+// Pick the resident configuration and part count for slice length S (S % 4 == 0 required).
+bool choose_resident(int64_t S, int* cfg_idx, int* P)
+{
+    if (S % 4 != 0) return false;
+    const int n = resident_cfg_count();
+    int ob, ov;
+    if (resident_override(&ob, &ov)) {
+        for (int i = 0; i < n; ++i) {
+            const ResidentCfg c = resident_cfg(i);
+            if (c.block == ob && c.vec == ov) {
+                const int64_t p = (S + c.part_len - 1) / c.part_len;
+                if (p > kMaxParts) return false;
+                *cfg_idx = i;
+                *P = (int)p;
+                return true;
+            }
+        }
+        return false;
+    }
+    // Slices up to 16K elements: one workgroup, the smallest configuration that holds it.
+    for (int i = 0; i < n; ++i) {
+        const ResidentCfg c = resident_cfg(i);
+        if (c.part_len >= S && c.block == 256) {
+            *cfg_idx = i;
+            *P = 1;
+            return true;
+        }
+    }
+    // Larger slices: 512-thread parts of 32K elements (two workgroups share a CU), then
+    // 1024-thread parts of 64K elements.
+    for (int i = 0; i < n; ++i) {
+        const ResidentCfg c = resident_cfg(i);
+        if (c.block < 512) continue;
+        const int64_t p = (S + c.part_len - 1) / c.part_len;
+        if (p <= kMaxParts) {
+            *cfg_idx = i;
+            *P = (int)p;
+            return true;
+        }
+    }
+    return false;
+}
+
+// Could any resident configuration (including an override) need the exchange regions?
+bool may_need_exchange(int64_t S)
+{
+    if (S % 4 != 0 || S <= 1024) return false;
+    const ResidentCfg big = resident_cfg(resident_cfg_count() - 1);
+    return S <= (int64_t)kMaxParts * big.part_len;
+}
+
+struct InormLayout {
+    size_t counters = 0, slots = 0, partials = 0, stats = 0, bytes = 0;
+    bool exchange = false;
+    SplitGeom sg;
+};
+
+InormLayout inorm_layout(int64_t N, int64_t C, int64_t S, bool vec)
+{
+    InormLayout L;
+    const int64_t slices = N * C;
+    size_t off = kHeaderBytes;
+    L.exchange = may_need_exchange(S);
+    if (L.exchange) {
+        L.counters = off;
+        off = align_up(off + (size_t)slices * kCounterStride, kWsAlign);
+        L.slots = off;
+        off = align_up(off + (size_t)slices * kMaxParts * 2 * sizeof(unsigned long long), kWsAlign);
+    }
+    L.sg = split_geometry(N, C, S, false, vec);
+    L.partials = off;
+    off = align_up(off + (size_t)(slices * L.sg.chunks) * sizeof(float2), kWsAlign);
+    L.stats = off;
+    off = align_up(off + (size_t)slices * sizeof(GroupStat), kWsAlign);
+    L.bytes = off;
+    return L;
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+nr_status check_workspace(void* ws, size_t have, size_t need, const char* fn)
+{
+    if (!ws) return fail(NR_ERR_WORKSPACE, "%s: workspace is NULL (need %zu bytes)", fn, need);
+    if (!aligned(ws, kWsAlign)) return fail(NR_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", fn);
+    if (have < need)
+        return fail(NR_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, have, need);
+    return NR_OK;
+}
+
+nr_status run_split(const SplitGeom& g, const float* x, float* y, float eps, const float* gamma,
+                    const float* beta, float out_scale, float* save_mean, float* save_invstd,
+                    float2* partials, GroupStat* stats, hipStream_t stream, const char* fn)
+{
+    if (g.slices * g.chunks > 0x7fffffffLL)
+        return fail(NR_ERR_UNSUPPORTED, "%s: %lld slices x %lld chunks exceed one launch", fn,
+                    (long long)g.slices, (long long)g.chunks);
+    hipError_t e = launch_split_partial(g, x, nullptr, partials, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_split_merge(g, x, nullptr, partials, eps, stats, save_mean, save_invstd, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_split_apply(g, x, y, stats, gamma, beta, out_scale, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return NR_OK;
+}
+
+size_t bn_layout(int64_t N, int64_t C, int64_t S, bool vec, SplitGeom* g, size_t* partials, size_t* stats)
+{
+    *g = split_geometry(N, C, S, true, vec);
+    size_t off = kHeaderBytes;
+    *partials = off;
+    off = align_up(off + (size_t)(g->slices * g->chunks) * sizeof(float2), kWsAlign);
+    *stats = off;
+    off = align_up(off + (size_t)C * sizeof(GroupStat), kWsAlign);
+    return off;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Conv chain planning.
+// ---------------------------------------------------------------------------------------------
+nr_status check_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
+{
+    if (!d) return fail(NR_ERR_INVALID_ARG, "%s: descriptor is NULL", fn);
+    if (d->spatial_dims != 2 && d->spatial_dims != 3)
+        return fail(NR_ERR_INVALID_ARG, "%s: spatial_dims must be 2 or 3", fn);
+    if (d->ksize != 3) return fail(NR_ERR_UNSUPPORTED, "%s: only ksize 3 is implemented (got %d)", fn, d->ksize);
+    if (d->N < 0 || d->C_in < 1 || d->C_out < 1)
+        return fail(NR_ERR_INVALID_ARG, "%s: need N >= 0, C_in >= 1, C_out >= 1", fn);
+    const int64_t D = d->spatial_dims == 3 ? d->in_d : 1;
+    if (d->in_h < 3 || d->in_w < 3 || (d->spatial_dims == 3 && d->in_d < 3))
+        return fail(NR_ERR_INVALID_ARG, "%s: input extent must be >= 3 along each spatial axis", fn);
+    if (d->norm != NR_NORM_BATCH_TRAIN && d->norm != NR_NORM_INSTANCE)
+        return fail(NR_ERR_INVALID_ARG, "%s: norm must be NR_NORM_BATCH_TRAIN or NR_NORM_INSTANCE", fn);
+    nr_status s = check_eps(d->eps, fn);
+    if (s != NR_OK) return s;
+    if (!std::isfinite(d->out_scale)) return fail(NR_ERR_INVALID_ARG, "%s: out_scale must be finite", fn);
+    if (d->clamp != 0 && d->clamp != 1) return fail(NR_ERR_INVALID_ARG, "%s: clamp must be 0 or 1", fn);
+    if (d->clamp && !(d->clamp_lo <= d->clamp_hi))
+        return fail(NR_ERR_INVALID_ARG, "%s: clamp_lo must be <= clamp_hi", fn);
+    if (d->reduce_max_c != 0 && d->reduce_max_c != 1)
+        return fail(NR_ERR_INVALID_ARG, "%s: reduce_max_c must be 0 or 1", fn);
+    if ((s = check_opt(d->pre_mul, "pre_mul", fn)) != NR_OK) return s;
+    if ((s = check_opt(d->gamma, "gamma", fn)) != NR_OK) return s;
+    if ((s = check_opt(d->beta, "beta", fn)) != NR_OK) return s;
+    if ((s = check_opt(d->post_mul, "post_mul", fn)) != NR_OK) return s;
+    ConvGeom c;
+    c.dims = d->spatial_dims;
+    c.N = d->N;
+    c.Cin = d->C_in;
+    c.Cout = d->C_out;
+    c.D = D;
+    c.H = d->in_h;
+    c.W = d->in_w;
+    c.OD = d->spatial_dims == 3 ? D - 2 : 1;
+    c.OH = d->in_h - 2;
+    c.OW = d->in_w - 2;
+    int64_t t = 0, sp = 0, nc = 0;
+    if (!mul_ok(c.OD, c.OH, &t) || !mul_ok(t, c.OW, &sp) || !mul_ok(c.N, c.Cout, &nc) ||
+        !mul_ok(nc, sp, &t) || !mul_ok(t, 4, &t))
+        return fail(NR_ERR_INVALID_ARG, "%s: output size overflows", fn);
+    int64_t in_t = 0;
+    if (!mul_ok(c.N, c.Cin, &in_t) || !mul_ok(in_t, D, &in_t) || !mul_ok(in_t, c.H, &in_t) ||
+        !mul_ok(in_t, c.W, &in_t) || !mul_ok(in_t, 4, &in_t))
+        return fail(NR_ERR_INVALID_ARG, "%s: input size overflows", fn);
+    c.SP = sp;
+    if (c.N > 65535 || (c.Cout + 15) / 16 > 65535 || (sp + 255) / 256 > 0x7fffffffLL)
+        return fail(NR_ERR_UNSUPPORTED, "%s: shape exceeds the launch grid limits", fn);
+    *g = c;
+    return NR_OK;
+}
+
+struct ChainLayout {
+    size_t cbuf = 0, partials = 0, stats = 0, bytes = 0;
+    SplitGeom sg;
+};
+
+ChainLayout chain_layout(const ConvGeom& g, bool batch)
+{
+    ChainLayout L;
+    size_t off = kHeaderBytes;
+    L.cbuf = off;
+    off = align_up(off + (size_t)(g.N * g.Cout * g.SP) * sizeof(float), kWsAlign);
+    L.sg = split_geometry(g.N, g.Cout, g.SP, batch, g.SP % 4 == 0);
+    L.partials = off;
+    off = align_up(off + (size_t)(L.sg.slices * L.sg.chunks) * sizeof(float2), kWsAlign);
+    L.stats = off;
+    off = align_up(off + (size_t)(batch ? g.Cout : g.N * g.Cout) * sizeof(GroupStat), kWsAlign);
+    L.bytes = off;
+    return L;
+}
+
+}  // namespace
+
+// =============================================================================================
+// Exported entry points.
+// =============================================================================================
+extern "C" {
+
+__attribute__((visibility("default"))) const char* nr_last_error(void) { return t_err.c_str(); }
+
+__attribute__((visibility("default"))) const char* nr_version(void) { return "normred 0.1.0 gfx950"; }
+
+__attribute__((visibility("default"))) size_t inorm_workspace_size(int64_t N, int64_t C, int64_t S)
+{
+    int64_t total = 0;
+    if (check_sizes(N, C, S, &total, "inorm_workspace_size") != NR_OK) return 0;
+    // the vector and scalar split geometries are identical in size
+    return inorm_layout(N, C, S, true).bytes;
+}
+
+__attribute__((visibility("default"))) nr_status inorm_forward_ex(
+    const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps, const float* gamma,
+    const float* beta, float* save_mean, float* save_invstd, void* workspace,
+    size_t workspace_bytes, int variant, hipStream_t stream)
+{
+    static const char* fn = "inorm_forward";
+    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
+    int64_t total = 0;
+    nr_status s = check_sizes(N, C, S, &total, fn);
+    if (s != NR_OK) return s;
+    if (!aligned(x, 4) || !aligned(y, 4)) return fail(NR_ERR_MISALIGNED, "%s: x and y must be 4-byte aligned", fn);
+    if (ranges_partially_overlap(x, y, total))
+        return fail(NR_ERR_INVALID_ARG, "%s: x and y overlap without being the same buffer", fn);
+    if ((gamma == nullptr) != (beta == nullptr))
+        return fail(NR_ERR_INVALID_ARG, "%s: gamma and beta must both be given or both be NULL", fn);
+    if ((s = check_eps(eps, fn)) != NR_OK) return s;
+    if ((s = check_opt(gamma, "gamma", fn)) != NR_OK) return s;
+    if ((s = check_opt(beta, "beta", fn)) != NR_OK) return s;
+    if ((s = check_opt(save_mean, "save_mean", fn)) != NR_OK) return s;
+    if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
+    if (variant != NR_VARIANT_AUTO && variant != NR_VARIANT_RESIDENT && variant != NR_VARIANT_SPLIT)
+        return fail(NR_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (total == 0) return NR_OK;  // empty batch: nothing to do
+
+    const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
+    const InormLayout L = inorm_layout(N, C, S, vec);
+    if ((s = check_workspace(workspace, workspace_bytes, L.bytes, fn)) != NR_OK) return s;
+
+    int cfg_idx = -1, P = 0;
+    const bool res_ok = vec && choose_resident(S, &cfg_idx, &P) && (P == 1 || L.exchange);
+    bool use_res = false;
+    if (variant == NR_VARIANT_RESIDENT) {
+        if (!res_ok)
+            return fail(NR_ERR_UNSUPPORTED,
+                        "%s: the resident variant needs 16-byte aligned x/y, S %% 4 == 0 and "
+                        "S <= %lld (S=%lld)", fn,
+                        (long long)kMaxParts * resident_cfg(resident_cfg_count() - 1).part_len,
+                        (long long)S);
+        use_res = true;
+    } else if (variant == NR_VARIANT_AUTO) {
+        use_res = res_ok;
+    }
+
+    if (use_res) {
+        const ResidentCfg cfg = resident_cfg(cfg_idx);
+        ResidentArgs a;
+        a.x = x;
+        a.y = y;
+        a.S = S;
+        a.slices = N * C;
+        a.C = (int32_t)(C > 0x7fffffff ? 0x7fffffff : C);
+        a.P = P;
+        a.eps = eps;
+        a.gamma = gamma;
+        a.beta = beta;
+        a.save_mean = save_mean;
+        a.save_invstd = save_invstd;
+        a.counters = L.exchange ? ws_at<uint32_t>(workspace, L.counters) : nullptr;
+        a.slots = L.exchange ? ws_at<unsigned long long>(workspace, L.slots) : nullptr;
+        a.flags = ws_at<uint32_t>(workspace, 0);
+        if (C > 0x7fffffff) return fail(NR_ERR_UNSUPPORTED, "%s: C too large for the resident variant", fn);
+        const hipError_t e = launch_resident(cfg, a, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
+    return run_split(L.sg, x, y, eps, gamma, beta, 1.0f, save_mean, save_invstd,
+                     ws_at<float2>(workspace, L.partials), ws_at<GroupStat>(workspace, L.stats),
+                     stream, fn);
+}
+
+__attribute__((visibility("default"))) nr_status inorm_forward(
+    const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps, const float* gamma,
+    const float* beta, float* save_mean, float* save_invstd, void* workspace,
+    size_t workspace_bytes, hipStream_t stream)
+{
+    return inorm_forward_ex(x, y, N, C, S, eps, gamma, beta, save_mean, save_invstd, workspace,
+                            workspace_bytes, NR_VARIANT_AUTO, stream);
+}
+
+__attribute__((visibility("default"))) size_t bn_train_workspace_size(int64_t N, int64_t C, int64_t S)
+{
+    int64_t total = 0;
+    if (N < 1 || check_sizes(N, C, S, &total, "bn_train_workspace_size") != NR_OK) return 0;
+    SplitGeom g;
+    size_t p, st;
+    return bn_layout(N, C, S, true, &g, &p, &st);
+}
+
+__attribute__((visibility("default"))) nr_status bn_train_forward(
+    const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps, const float* gamma,
+    const float* beta, float out_scale, float* save_mean, float* save_invstd, void* workspace,
+    size_t workspace_bytes, hipStream_t stream)
+{
+    static const char* fn = "bn_train_forward";
+    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
+    if (N < 1) return fail(NR_ERR_INVALID_ARG, "%s: batch statistics need N >= 1", fn);
+    int64_t total = 0;
+    nr_status s = check_sizes(N, C, S, &total, fn);
+    if (s != NR_OK) return s;
+    if (!aligned(x, 4) || !aligned(y, 4)) return fail(NR_ERR_MISALIGNED, "%s: x and y must be 4-byte aligned", fn);
+    if (ranges_partially_overlap(x, y, total))
+        return fail(NR_ERR_INVALID_ARG, "%s: x and y overlap without being the same buffer", fn);
+    if ((gamma == nullptr) != (beta == nullptr))
+        return fail(NR_ERR_INVALID_ARG, "%s: gamma and beta must both be given or both be NULL", fn);
+    if ((s = check_eps(eps, fn)) != NR_OK) return s;
+    if (!std::isfinite(out_scale)) return fail(NR_ERR_INVALID_ARG, "%s: out_scale must be finite", fn);
+    if ((s = check_opt(gamma, "gamma", fn)) != NR_OK) return s;
+    if ((s = check_opt(beta, "beta", fn)) != NR_OK) return s;
+    if ((s = check_opt(save_mean, "save_mean", fn)) != NR_OK) return s;
+    if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
+    if (total == 0) return NR_OK;  // no channels
+    const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
+    SplitGeom g;
+    size_t off_p, off_s;
+    const size_t need = bn_layout(N, C, S, vec, &g, &off_p, &off_s);
+    if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
+    return run_split(g, x, y, eps, gamma, beta, out_scale, save_mean, save_invstd,
+                     ws_at<float2>(workspace, off_p), ws_at<GroupStat>(workspace, off_s), stream, fn);
+}
+
+__attribute__((visibility("default"))) size_t conv_norm_epilogue_workspace_size(const nr_conv_norm_desc* d)
+{
+    ConvGeom g;
+    if (check_desc(d, &g, "conv_norm_epilogue_workspace_size") != NR_OK) return 0;
+    return chain_layout(g, d->norm == NR_NORM_BATCH_TRAIN).bytes;
+}
+
+__attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
+    const nr_conv_norm_desc* d, const float* x, const float* w, const float* b, float* out,
+    void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    static const char* fn = "conv_norm_epilogue_forward";
+    ConvGeom g;
+    nr_status s = check_desc(d, &g, fn);
+    if (s != NR_OK) return s;
+    if (!x || !w || !out) return fail(NR_ERR_INVALID_ARG, "%s: x, w and out must be non-NULL", fn);
+    if (g.N == 0) return NR_OK;  // empty batch
+    if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (b && !aligned(b, 4)))
+        return fail(NR_ERR_MISALIGNED, "%s: tensors must be 4-byte aligned", fn);
+    const bool batch = d->norm == NR_NORM_BATCH_TRAIN;
+    const ChainLayout L = chain_layout(g, batch);
+    if ((s = check_workspace(workspace, workspace_bytes, L.bytes, fn)) != NR_OK) return s;
+    if (L.sg.slices * L.sg.chunks > 0x7fffffffLL)
+        return fail(NR_ERR_UNSUPPORTED, "%s: too many statistics chunks for one launch", fn);
+
+    float* c = ws_at<float>(workspace, L.cbuf);
+    float2* partials = ws_at<float2>(workspace, L.partials);
+    GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
+    hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_split_partial(L.sg, c, d->pre_mul, partials, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_split_merge(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    ChainArgs a;
+    a.c = c;
+    a.out = out;
+    a.N = g.N;
+    a.Cout = g.Cout;
+    a.SP = g.SP;
+    a.batch = batch;
+    a.stats = stats;
+    a.pre_mul = d->pre_mul;
+    a.gamma = d->gamma;
+    a.beta = d->beta;
+    a.out_scale = d->out_scale;
+    a.clamp = d->clamp;
+    a.lo = d->clamp_lo;
+    a.hi = d->clamp_hi;
+    a.post_mul = d->post_mul;
+    a.reduce_max_c = d->reduce_max_c;
+    e = launch_chain_apply(a, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return NR_OK;
+}
+
+__attribute__((visibility("default"))) nr_status nr_workspace_clear(void* workspace, size_t bytes,
+                                                                    hipStream_t stream)
+{
+    if (!workspace) return fail(NR_ERR_INVALID_ARG, "nr_workspace_clear: workspace is NULL");
+    if (bytes == 0) return NR_OK;
+    const hipError_t e = launch_fill_zero(workspace, bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "nr_workspace_clear");
+    return NR_OK;
+}
+
+__attribute__((visibility("default"))) nr_status nr_workspace_check(void* workspace, size_t bytes,
+                                                                    hipStream_t stream,
+                                                                    uint32_t* flags_out)
+{
+    static const char* fn = "nr_workspace_check";
+    if (!workspace || !flags_out) return fail(NR_ERR_INVALID_ARG, "%s: NULL argument", fn);
+    if (bytes < kHeaderBytes) return fail(NR_ERR_WORKSPACE, "%s: workspace smaller than its header", fn);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    uint32_t flags = 0, zero = 0;
+    e = hipMemcpy(&flags, workspace, sizeof(flags), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (flags) {
+        e = hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    *flags_out = flags;
+    return NR_OK;
+}
+
+__attribute__((visibility("default"))) nr_status nr_stream_copy(const float* src, float* dst, int64_t n,
+                                                                hipStream_t stream)
+{
+    if (!src || !dst || n < 0) return fail(NR_ERR_INVALID_ARG, "nr_stream_copy: bad arguments");
+    if (!aligned(src, 4) || !aligned(dst, 4)) return fail(NR_ERR_MISALIGNED, "nr_stream_copy: misaligned");
+    if (ranges_partially_overlap(src, dst, n) || (src == dst && n > 0))
+        return fail(NR_ERR_INVALID_ARG, "nr_stream_copy: src and dst overlap");
+    const hipError_t e = launch_stream_copy(src, dst, n, stream);
+    if (e != hipSuccess) return hip_fail(e, "nr_stream_copy");
+    return NR_OK;
+}
+
+}  // extern "C"

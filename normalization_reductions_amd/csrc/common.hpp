@@ -1,0 +1,113 @@
+// common.hpp -- device building blocks shared by the gfx950 kernels of libnormred.
+//
+// Statistics are carried as (count, mean, M2) with M2 = sum of squared deviations from the
+// mean. Partial statistics are combined with the pairwise (Chan et al.) update that the IN2d
+// page (task l1_p34, its Welford kernel design) and the IN3d page (task l2_p79, its shared-
+// memory tree of Welford states) both use:
+//     n = na + nb,  d = mean_b - mean_a,  mean = mean_a + d*nb/n,  M2 = M2a + M2b + d^2*na*nb/n
+// with an empty state (n = 0) acting as the identity.
+//
+// Wave reductions are written for 64-lane wavefronts: a butterfly over lane distances
+// 1, 2, 4, ..., 32 in which both partners always merge (lower lane, upper lane) in that order,
+// so every lane of a group ends with bit-identical results and the combine order is a fixed
+// balanced tree over consecutive lanes -- deterministic from run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nr {
+
+constexpr int kWave = 64;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct Stat {
+    float n;     // element count (exact in fp32 up to 2^24)
+    float mean;  // mean of the values (relative to the caller's pivot)
+    float m2;    // sum of squared deviations from `mean`
+};
+
+__device__ __forceinline__ Stat stat_empty() { return Stat{0.f, 0.f, 0.f}; }
+
+// Pairwise merge; `a` is always the lower-indexed range, `b` the higher one.
+__device__ __forceinline__ Stat chan_merge(Stat a, Stat b)
+{
+    const float n = a.n + b.n;
+    const float f = n > 0.f ? b.n / n : 0.f;  // weight of b
+    const float d = b.mean - a.mean;
+    Stat r;
+    r.n = n;
+    r.mean = fmaf(d, f, a.mean);
+    r.m2 = a.m2 + b.m2 + d * d * a.n * f;
+    return r;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Butterfly over lane distances 1 .. WIDTH/2 (WIDTH a power of two <= 64). After it, every
+// lane of each aligned group of WIDTH lanes holds the merge of the group, combined as a
+// balanced tree over consecutive lanes.
+template <int WIDTH>
+__device__ __forceinline__ Stat wave_merge(Stat s)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < WIDTH; off <<= 1) {
+        Stat o;
+        o.n = __shfl_xor(s.n, off);
+        o.mean = __shfl_xor(s.mean, off);
+        o.m2 = __shfl_xor(s.m2, off);
+        const bool upper = (lane & off) != 0;
+        s = upper ? chan_merge(o, s) : chan_merge(s, o);
+    }
+    return s;
+}
+
+// Plain-sum butterfly (all lanes end with the same fixed-order sum).
+template <int WIDTH>
+__device__ __forceinline__ float wave_sum(float v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < WIDTH; off <<= 1) {
+        const float o = __shfl_xor(v, off);
+        v = (lane & off) ? (o + v) : (v + o);
+    }
+    return v;
+}
+
+// Streaming 16-byte accesses: each byte of x and y is touched once, so hint non-temporal.
+__device__ __forceinline__ f4 ld_stream(const f4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(f4* p, f4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ float ld_stream1(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream1(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
+// Exchange words between co-resident workgroups: 64-bit, tagged with an epoch in the high
+// half and an fp32 payload in the low half. They are only ever accessed with relaxed
+// agent-scope atomics, so each word is read whole and coherently across the XCDs' L2s;
+// a reader accepts a word only when its tag equals the epoch it waits for.
+__device__ __forceinline__ void xchg_store(unsigned long long* p, uint32_t epoch, float v)
+{
+    const unsigned long long w =
+        ((unsigned long long)epoch << 32) | (unsigned long long)__float_as_uint(v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long xchg_load(unsigned long long* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Upper bound on polling rounds in a co-residency wait; with ~1 us of sleep per round this is
+// far beyond any legitimate wait (all waiters are co-resident by construction), and it keeps
+// a broken launch from spinning forever: the wait gives up and raises a sticky flag.
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kFlagSpinTimeout = 1u;
+
+__device__ __forceinline__ void raise_flag(uint32_t* flags, uint32_t bit)
+{
+    __hip_atomic_fetch_or(flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace nr

@@ -1,0 +1,125 @@
+// internal.hpp -- host-side interfaces between the C ABI layer (abi.cpp) and the kernel
+// launchers (*.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nr {
+
+// ---------------------------------------------------------------------------------------------
+// Workspace regions (byte offsets inside the caller's workspace; every region 256-B aligned).
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kWsAlign = 256;
+constexpr size_t kHeaderBytes = 256;     // uint32 flags at offset 0
+constexpr int kMaxParts = 16;            // parts per slice in the co-resident variant
+constexpr size_t kCounterStride = 128;   // bytes per slice epoch counter (one cache line)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------------------------
+// Read-once ("resident") instance norm: each slice split over P co-resident workgroups, each
+// holding its part in registers.
+// ---------------------------------------------------------------------------------------------
+struct ResidentCfg {
+    int block;     // threads per workgroup
+    int vec;       // float4 registers per thread
+    int part_len;  // elements per part = block * 4 * vec
+};
+
+// The configurations compiled into the library, ascending by part length.
+int resident_cfg_count();
+ResidentCfg resident_cfg(int i);
+
+struct ResidentArgs {
+    const float* x;
+    float* y;
+    int64_t S;        // slice length; S % 4 == 0, x and y 16-B aligned
+    int64_t slices;   // N*C
+    int32_t C;
+    int32_t P;        // parts per slice, 1..kMaxParts
+    float eps;
+    const float* gamma;
+    const float* beta;
+    float* save_mean;
+    float* save_invstd;
+    uint32_t* counters;          // [slices] epoch counters, kCounterStride apart
+    unsigned long long* slots;   // [slices][kMaxParts][2] tagged exchange words
+    uint32_t* flags;             // sticky error word
+};
+
+// Largest grid the kernel can have fully co-resident (0 if the configuration is unknown).
+int resident_max_grid(const ResidentCfg& cfg);
+hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Streaming split path: partial statistics per (slice, chunk) -> fixed-order merge per group
+// -> apply. Groups are slices (instance norm) or channels (batch norm).
+// ---------------------------------------------------------------------------------------------
+struct SplitGeom {
+    int64_t S;        // slice length
+    int64_t slices;   // N*C
+    int64_t C;        // channels (slice's channel = slice % C)
+    int64_t chunk;    // elements per chunk (multiple of 4 * block), last chunk may be shorter
+    int64_t chunks;   // ceil(S / chunk)
+    bool batch;       // true: group = channel over all n; false: group = slice
+    bool vec;         // 16-B path (aligned pointers and S % 4 == 0)
+};
+
+struct GroupStat {    // per group, written by the merge step
+    float pivot;      // the value the statistics are taken relative to
+    float mean_d;     // mean - pivot
+    float rstd;       // 1 / sqrt(var + eps)
+    float pad;
+};
+
+SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec);
+
+hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
+                                float2* partials, hipStream_t stream);
+hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
+                              const float2* partials, float eps, GroupStat* stats,
+                              float* save_mean, float* save_invstd, hipStream_t stream);
+hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
+                              const GroupStat* stats, const float* gamma, const float* beta,
+                              float out_scale, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Convolution producer and the chain epilogue.
+// ---------------------------------------------------------------------------------------------
+struct ConvGeom {
+    int dims;                  // 2 or 3
+    int64_t N, Cin, Cout;
+    int64_t D, H, W;           // input extent (D = 1 for 2-D)
+    int64_t OD, OH, OW, SP;    // output extent, SP = OD*OH*OW
+};
+
+hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
+                          float* c, hipStream_t stream);
+
+struct ChainArgs {
+    const float* c;        // [N, Cout, SP] conv output
+    float* out;            // [N, SP] (max over channels) or [N, Cout, SP]
+    int64_t N, Cout, SP;
+    bool batch;            // statistics per channel (true) or per (n, k) (false)
+    const GroupStat* stats;
+    const float* pre_mul;
+    const float* gamma;
+    const float* beta;
+    float out_scale;
+    int clamp;
+    float lo, hi;
+    const float* post_mul;
+    int reduce_max_c;
+};
+
+hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Utilities.
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+
+}  // namespace nr

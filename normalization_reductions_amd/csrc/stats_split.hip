@@ -1,0 +1,243 @@
+// stats_split.hip -- streaming statistics for any slice length or alignment, and for batch
+// normalization, on gfx950.
+//
+// Operations: IN2d page (task l1_p34), statement of the op (instance statistics per (n, c));
+// BN page (task l2_p73), opening analysis (training-mode batch statistics per channel over
+// (n, h, w)). Both reduce to "mean and biased variance of a group of slices": a group is one
+// slice for instance norm and the N slices of one channel for batch norm.
+//
+// Three kernels, each deterministic:
+//   1. partial: one workgroup per (slice, chunk) streams its chunk once and writes the chunk's
+//      (mean, M2) relative to the group's pivot. Per thread, values are taken 16 at a time from
+//      16-byte loads, reduced by the two-pass formula over registers and folded into a running
+//      state with the pairwise (Chan) merge -- the batched form of the per-element Welford
+//      update both pages use, with one division per 16 values instead of one per value.
+//   2. merge: one wave per group merges all of the group's chunk partials in a fixed order
+//      (the page's split-slice scheme with a final fixed-order combine instead of float
+//      atomics) and writes pivot, mean - pivot and 1/sqrt(var + eps).
+//   3. apply: one workgroup per (slice, chunk) normalizes its chunk (second read of x).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace nr {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kNW = kBlock / kWave;
+
+__device__ __forceinline__ int64_t chunk_len(const SplitGeom& g, int64_t ch)
+{
+    const int64_t r = g.S - ch * g.chunk;
+    return r < g.chunk ? r : g.chunk;
+}
+
+// Index of the slice holding a group's pivot (its first element).
+// (instance: the slice itself; batch: channel c's first slice, n = 0, has index c)
+__device__ __forceinline__ int64_t pivot_slice(int64_t group) { return group; }
+
+__device__ __forceinline__ int64_t group_of(const SplitGeom& g, int64_t slice)
+{
+    return g.batch ? slice % g.C : slice;
+}
+
+// Fold a batch of values into a running state. d[0..n) hold the (pivot-shifted) values and
+// d[n..16) are zero; indices are static so the batch stays in registers.
+__device__ __forceinline__ Stat fold16(Stat run, const float (&d)[16], int n)
+{
+    if (n <= 0) return run;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += d[i];
+    const float fn = (float)n;
+    const float m = s / fn;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (i < n) q = fmaf(d[i] - m, d[i] - m, q);
+    return chan_merge(run, Stat{fn, m, q});
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, const float* x,
+                                                               const float* pre_mul,
+                                                               float2* partials)
+{
+    __shared__ Stat wstat[kNW];
+    const int64_t wg = blockIdx.x;
+    const int64_t slice = wg / g.chunks;
+    const int64_t ch = wg - slice * g.chunks;
+    const int64_t c = slice % g.C;
+    const float m = pre_mul ? pre_mul[c] : 1.f;
+    const float K = x[pivot_slice(group_of(g, slice)) * g.S] * m;
+    const int64_t start = ch * g.chunk;
+    const int64_t len = chunk_len(g, ch);
+    const float* xs = x + slice * g.S + start;
+    const int tid = threadIdx.x;
+
+    Stat st = stat_empty();
+    float d[16];
+    if (VEC) {
+        const f4* xv = reinterpret_cast<const f4*>(xs);
+        const int64_t nv = len >> 2;
+        for (int64_t i0 = 0; i0 < nv; i0 += 4 * kBlock) {
+            int n = 0;  // valid entries form a prefix: j < some bound
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = i0 + j * kBlock + tid;
+                f4 t = f4{0.f, 0.f, 0.f, 0.f};
+                if (i < nv) {
+                    t = ld_stream(xv + i) * m - K;
+                    n += 4;
+                }
+                d[4 * j + 0] = t.x;
+                d[4 * j + 1] = t.y;
+                d[4 * j + 2] = t.z;
+                d[4 * j + 3] = t.w;
+            }
+            st = fold16(st, d, n);
+        }
+    } else {
+        for (int64_t i0 = 0; i0 < len; i0 += 16 * kBlock) {
+            int n = 0;  // valid entries form a prefix
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t i = i0 + j * kBlock + tid;
+                d[j] = 0.f;
+                if (i < len) {
+                    d[j] = ld_stream1(xs + i) * m - K;
+                    ++n;
+                }
+            }
+            st = fold16(st, d, n);
+        }
+    }
+
+    st = wave_merge<kWave>(st);
+    if (lane_id() == 0) wstat[tid / kWave] = st;
+    __syncthreads();
+    if (tid < kWave) {
+        Stat w = tid < kNW ? wstat[tid] : stat_empty();
+        w = wave_merge<kNW>(w);
+        if (tid == 0) partials[wg] = make_float2(w.mean, w.m2);
+    }
+}
+
+// One wave per group.
+__global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const float* x,
+                                                            const float* pre_mul,
+                                                            const float2* partials, float eps,
+                                                            GroupStat* stats, float* save_mean,
+                                                            float* save_invstd)
+{
+    const int64_t grp = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t members = g.batch ? g.slices / g.C : 1;
+    const int64_t total = members * g.chunks;
+
+    Stat st = stat_empty();
+    for (int64_t q = lane; q < total; q += kWave) {
+        const int64_t mem = q / g.chunks;
+        const int64_t ch = q - mem * g.chunks;
+        const int64_t slice = g.batch ? mem * g.C + grp : grp;
+        const float2 p = partials[slice * g.chunks + ch];
+        st = chan_merge(st, Stat{(float)chunk_len(g, ch), p.x, p.y});
+    }
+    st = wave_merge<kWave>(st);
+    if (lane == 0) {
+        const int64_t c = grp % g.C;
+        const float m = pre_mul ? pre_mul[c] : 1.f;
+        const float K = x[pivot_slice(grp) * g.S] * m;
+        const float rstd = rsqrtf(st.m2 / st.n + eps);
+        stats[grp] = GroupStat{K, st.mean, rstd, 0.f};
+        if (save_mean) save_mean[grp] = K + st.mean;
+        if (save_invstd) save_invstd[grp] = rstd;
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void split_apply_kernel(SplitGeom g, const float* x, float* y,
+                                                             const GroupStat* stats,
+                                                             const float* gamma,
+                                                             const float* beta, float out_scale)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t slice = wg / g.chunks;
+    const int64_t ch = wg - slice * g.chunks;
+    const int64_t c = slice % g.C;
+    const GroupStat s = stats[group_of(g, slice)];
+    const float A = s.rstd * (gamma ? gamma[c] : 1.f) * out_scale;
+    const float B = (beta ? beta[c] : 0.f) * out_scale;
+    const float K = s.pivot, md = s.mean_d;
+    const int64_t start = ch * g.chunk;
+    const int64_t len = chunk_len(g, ch);
+    const int64_t off = slice * g.S + start;
+    const int tid = threadIdx.x;
+    if (VEC) {
+        const f4* xv = reinterpret_cast<const f4*>(x + off);
+        f4* yv = reinterpret_cast<f4*>(y + off);
+        const int64_t nv = len >> 2;
+        for (int64_t i = tid; i < nv; i += kBlock) st_stream(yv + i, ((ld_stream(xv + i) - K) - md) * A + B);
+    } else {
+        for (int64_t i = tid; i < len; i += kBlock)
+            st_stream1(y + off + i, ((ld_stream1(x + off + i) - K) - md) * A + B);
+    }
+}
+
+}  // namespace
+
+SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec)
+{
+    SplitGeom g;
+    g.S = S;
+    g.slices = N * C;
+    g.C = C;
+    g.batch = batch;
+    g.vec = vec;
+    // Aim for >= ~2048 workgroups in flight, with chunks of at least 4096 elements and a
+    // multiple of 4 * 256 so every chunk starts 16-byte aligned.
+    const int64_t sl = g.slices > 0 ? g.slices : 1;  // an empty batch still gets a valid shape
+    const int64_t want_chunks = (2048 + sl - 1) / sl;
+    int64_t chunk = (S + want_chunks - 1) / want_chunks;
+    chunk = (chunk + 1023) / 1024 * 1024;
+    if (chunk < 4096) chunk = 4096;
+    const int64_t s_up = (S + 1023) / 1024 * 1024;
+    if (chunk > s_up) chunk = s_up;
+    g.chunk = chunk;
+    g.chunks = (S + chunk - 1) / chunk;
+    return g;
+}
+
+hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
+                                float2* partials, hipStream_t stream)
+{
+    const int64_t grid = g.slices * g.chunks;
+    if (g.vec)
+        split_partial_kernel<true><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, pre_mul, partials);
+    else
+        split_partial_kernel<false><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, pre_mul, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
+                              const float2* partials, float eps, GroupStat* stats,
+                              float* save_mean, float* save_invstd, hipStream_t stream)
+{
+    const int64_t groups = g.batch ? g.C : g.slices;
+    split_merge_kernel<<<dim3((unsigned)groups), dim3(kWave), 0, stream>>>(
+        g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
+                              const GroupStat* stats, const float* gamma, const float* beta,
+                              float out_scale, hipStream_t stream)
+{
+    const int64_t grid = g.slices * g.chunks;
+    if (g.vec)
+        split_apply_kernel<true><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, y, stats, gamma, beta, out_scale);
+    else
+        split_apply_kernel<false><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, y, stats, gamma, beta, out_scale);
+    return hipGetLastError();
+}
+
+}  // namespace nr

@@ -1,0 +1,392 @@
+"""Parity of the HIP path against the fp64 oracle (needs an MI355X: run with -m gpu).
+
+Bar: max |gpu - oracle| <= 1e-4 over every compared output element (fp32 outputs), the
+tolerance the workloads state; bit-identical results across repeated runs; the workspace's
+error flags stay clear. All inputs come from the seeded generators in synth/.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def nra(dev):
+    import normalization_reductions_amd as m
+
+    m._lib.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle._load()
+    return oracle
+
+
+def T(a, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def H(t):
+    import torch
+
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------------------------------
+# Instance norm: the three InstanceNorm2d workloads
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_inorm_workload1(dev, nra, orc, variant):
+    inp = synth.host_inputs(1)
+    y = nra.inorm_forward(T(inp["x"], dev), eps=inp["eps"], variant=variant)
+    err = maxerr(H(y), orc.instance_norm(inp["x"], eps=inp["eps"]))
+    _log("inorm x[2,4,32,32] variant %d: max_abs_err %.3e" % (variant, err))
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("variant", [0, 2])
+def test_inorm_workload2_full(dev, nra, orc, variant):
+    inp = synth.host_inputs(2)
+    x = T(inp["x"], dev)
+    n, c = x.shape[:2]
+    import torch
+
+    sm = torch.empty(n * c, device=dev)
+    si = torch.empty(n * c, device=dev)
+    y = nra.inorm_forward(x, eps=inp["eps"], save_mean=sm, save_invstd=si, variant=variant)
+    ref, mean, var = orc.instance_norm(inp["x"], eps=inp["eps"], with_stats=True)
+    err = maxerr(H(y), ref)
+    _log("inorm x[16,64,256,256] (offsets +-100) variant %d: max_abs_err %.3e" % (variant, err))
+    assert err <= TOL
+    np.testing.assert_allclose(H(sm), mean.ravel(), rtol=2e-7, atol=2e-5)
+    np.testing.assert_allclose(H(si), 1.0 / np.sqrt(var.ravel() + 1e-5), rtol=1e-5)
+    y2 = nra.inorm_forward(x, eps=inp["eps"], variant=variant)
+    assert torch.equal(y, y2)
+
+
+@pytest.fixture(scope="module")
+def w3(dev):
+    import torch
+
+    x = synth.device_inputs_cfg3(dev)["x"]
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+def _sample_slices(total, k, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    fixed = [0, 1, 63, 64, 511, 512, total // 2, total - 2, total - 1]
+    rest = g.choice(total, size=k, replace=False).tolist()
+    return sorted(set(fixed + rest))
+
+
+@pytest.mark.parametrize("variant", [0, 2])
+def test_inorm_workload3_full_size(dev, nra, orc, w3, variant):
+    import torch
+
+    x = w3
+    N, C = x.shape[:2]
+    S = x.shape[2] * x.shape[3]
+    sm = torch.empty(N * C, device=dev)
+    si = torch.empty(N * C, device=dev)
+    ws = torch.zeros(nra.inorm_workspace_size(N, C, S), dtype=torch.uint8, device=dev)
+    y = nra.inorm_forward(x, eps=1e-5, save_mean=sm, save_invstd=si, workspace=ws, variant=variant)
+    torch.cuda.synchronize()
+    assert nra.workspace_check(ws) == 0
+
+    # sampled slices against the oracle, element by element
+    idx = _sample_slices(N * C, 40, 77)
+    xs = x.view(N * C, S)[idx].cpu().numpy()
+    ys = y.view(N * C, S)[idx].cpu().numpy()
+    ref, mean, var = orc.instance_norm_slices(xs, eps=1e-5, with_stats=True)
+    err = maxerr(ys, ref)
+    _log("inorm x[112,64,512,512] variant %d: %d sampled slices, max_abs_err %.3e"
+         % (variant, len(idx), err))
+    assert err <= TOL
+    np.testing.assert_allclose(H(sm)[idx], mean, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(H(si)[idx], 1.0 / np.sqrt(var + 1e-5), rtol=1e-5)
+
+    # every slice: output mean 0 and variance var/(var+eps) (closed form of the op)
+    yv = y.view(N * C, S)
+    var_all = (1.0 / si.double() ** 2) - 1e-5
+    for lo in range(0, N * C, 512):
+        blk = yv[lo:lo + 512].double()
+        m = blk.mean(dim=1)
+        v = blk.var(dim=1, unbiased=False)
+        assert float(m.abs().max()) < 1e-5
+        expect = var_all[lo:lo + 512] / (var_all[lo:lo + 512] + 1e-5)
+        assert float((v - expect).abs().max()) < 2e-5
+
+    y2 = nra.inorm_forward(x, eps=1e-5, workspace=ws, variant=variant)
+    assert torch.equal(y, y2)
+    assert nra.workspace_check(ws) == 0
+    del y, y2
+
+
+# ------------------------------------------------------------------------------------------
+# Instance norm: every compiled read-once configuration, ragged parts, edge shapes
+# ------------------------------------------------------------------------------------------
+RESIDENT_CASES = [
+    # (block, vec, S): P = ceil(S / (block*4*vec)) covers 1, ragged 3, and the 16-part maximum
+    (256, 1, 1024), (256, 1, 3000), (256, 1, 16384),
+    (256, 2, 2048), (256, 2, 6148),
+    (256, 4, 4096), (256, 4, 40960),
+    (256, 8, 8192), (256, 8, 20000),
+    (256, 16, 16384), (256, 16, 12600), (256, 16, 40000),
+    (512, 16, 32768), (512, 16, 262144), (512, 16, 65540), (512, 16, 524288),
+    (1024, 16, 65536), (1024, 16, 1048576), (1024, 16, 200004),
+]
+
+
+@pytest.mark.parametrize("block,vec,S", RESIDENT_CASES)
+def test_inorm_resident_configurations(dev, nra, orc, monkeypatch, block, vec, S):
+    import torch
+
+    monkeypatch.setenv("NORMRED_RESIDENT_CFG", "%d,%d" % (block, vec))
+    nc = max(2, min(24, (8 << 20) // S))
+    x = synth.per_slice_affine_normal((nc, 1, S), 1000 + S, (0.1, 10.0), (-100.0, 100.0))
+    xt = T(x, dev)
+    ws = torch.zeros(nra.inorm_workspace_size(nc, 1, S), dtype=torch.uint8, device=dev)
+    y = nra.inorm_forward(xt, variant=nra.NR_VARIANT_RESIDENT, workspace=ws)
+    err = maxerr(H(y), orc.instance_norm(x))
+    _log("resident block %d vec %d S %d slices %d: max_abs_err %.3e" % (block, vec, S, nc, err))
+    assert err <= TOL
+    assert nra.workspace_check(ws) == 0
+    y2 = nra.inorm_forward(xt, variant=nra.NR_VARIANT_RESIDENT, workspace=ws)
+    assert torch.equal(y, y2)
+
+
+EDGE_SHAPES = [(1, 1, 1), (3, 2, 5), (2, 3, 1023), (1, 1, 4), (2, 2, 65540), (1, 3, 262148),
+               (4, 2, 100000), (1, 1, 1048576), (2, 1, 1048580), (5, 7, 12600), (1, 1, 7)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES)
+@pytest.mark.parametrize("variant", [0, 2])
+def test_inorm_edge_shapes(dev, nra, orc, shape, variant):
+    x = synth.per_slice_affine_normal(shape, 7 + shape[2], (0.1, 10.0), (-100.0, 100.0))
+    y = nra.inorm_forward(T(x, dev), variant=variant)
+    err = maxerr(H(y), orc.instance_norm(x))
+    _log("inorm edge %s variant %d: max_abs_err %.3e" % (shape, variant, err))
+    assert err <= TOL
+
+
+def test_inorm_empty_batch(dev, nra):
+    import torch
+
+    x = torch.empty((0, 4, 16, 16), device=dev)
+    y = nra.inorm_forward(x)
+    assert y.shape == x.shape
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_inorm_constant_slices_are_exactly_zero(dev, nra, variant):
+    import torch
+
+    vals = torch.tensor([0.0, 3.25, -1234.5, 1e6, 7.0, -0.5], device=dev)
+    x = vals.view(2, 3, 1).expand(2, 3, 65536).contiguous()
+    y = nra.inorm_forward(x, variant=variant)
+    torch.cuda.synchronize()
+    assert bool((y == 0).all())
+
+
+def test_inorm_large_offset_small_spread(dev, nra, orc):
+    x = synth.per_slice_affine_normal((2, 4, 256, 256), 5, (0.01, 0.01), (1e4, 1e4))
+    y = nra.inorm_forward(T(x, dev))
+    err = maxerr(H(y), orc.instance_norm(x))
+    _log("inorm offset 1e4, spread 1e-2: max_abs_err %.3e" % err)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("S", [1024, 65536, 262144, 1000])
+def test_inorm_affine_inplace_stats(dev, nra, orc, S):
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(S))
+    N, C = 3, 5
+    x = synth.per_slice_affine_normal((N, C, S), 99, (0.5, 2.0), (-3.0, 3.0))
+    gamma = g.uniform(0.5, 1.5, C).astype(np.float32)
+    beta = g.uniform(-1, 1, C).astype(np.float32)
+    xt = T(x, dev)
+    sm = torch.empty(N * C, device=dev)
+    si = torch.empty(N * C, device=dev)
+    nra.inorm_forward(xt, xt, gamma=T(gamma, dev), beta=T(beta, dev), save_mean=sm,
+                      save_invstd=si)  # in place
+    ref, mean, var = orc.instance_norm(x, gamma=gamma, beta=beta, with_stats=True)
+    err = maxerr(H(xt), ref)
+    _log("inorm affine in-place S=%d: max_abs_err %.3e" % (S, err))
+    assert err <= TOL
+    np.testing.assert_allclose(H(sm), mean.ravel(), rtol=1e-6, atol=2e-6)
+    np.testing.assert_allclose(H(si), 1.0 / np.sqrt(var.ravel() + 1e-5), rtol=1e-5)
+
+
+def test_inorm_unaligned_and_side_stream(dev, nra, orc):
+    import torch
+
+    N, C, S = 2, 3, 4096
+    x = synth.per_slice_affine_normal((N, C, S), 123, (0.5, 2.0), (-3.0, 3.0))
+    buf = torch.empty(N * C * S + 1, device=dev)
+    buf[1:] = T(x, dev).view(-1)
+    xu = buf[1:].view(N, C, S)  # 4-byte offset: not 16-byte aligned
+    assert xu.data_ptr() % 16 != 0
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        y = nra.inorm_forward(xu)
+    s.synchronize()
+    err = maxerr(y.cpu().numpy(), orc.instance_norm(x))
+    assert err <= TOL
+    with pytest.raises(nra.NormredError):
+        nra.inorm_forward(xu, variant=nra.NR_VARIANT_RESIDENT)
+
+
+# ------------------------------------------------------------------------------------------
+# Training-mode batch norm
+# ------------------------------------------------------------------------------------------
+BN_SHAPES = [(128, 64, 3844), (1, 3, 1), (5, 2, 7), (2, 4, 4100), (3, 1, 100000), (64, 16, 1)]
+
+
+@pytest.mark.parametrize("shape", BN_SHAPES)
+def test_bn_train(dev, nra, orc, shape):
+    import torch
+
+    N, C, S = shape
+    g = np.random.Generator(np.random.PCG64(N * 1000 + C))
+    z = g.standard_normal(shape).astype(np.float32)
+    x = (z * g.uniform(0.1, 3, (1, C, 1)) + g.uniform(-5, 5, (1, C, 1))).astype(np.float32)
+    gamma = g.uniform(0.5, 1.5, C).astype(np.float32)
+    beta = g.uniform(-0.5, 0.5, C).astype(np.float32)
+    sm = torch.empty(C, device=dev)
+    si = torch.empty(C, device=dev)
+    xt = T(x, dev)
+    y = nra.bn_train_forward(xt, gamma=T(gamma, dev), beta=T(beta, dev), out_scale=2.0,
+                             save_mean=sm, save_invstd=si)
+    ref, mean, var = orc.batch_norm_train(x, gamma=gamma, beta=beta, scale=2.0, with_stats=True)
+    err = maxerr(H(y), ref)
+    _log("bn_train %s: max_abs_err %.3e" % (shape, err))
+    assert err <= TOL
+    np.testing.assert_allclose(H(sm), mean, rtol=1e-6, atol=2e-6)
+    np.testing.assert_allclose(H(si), 1.0 / np.sqrt(var + 1e-5), rtol=1e-5)
+    y2 = nra.bn_train_forward(xt, gamma=T(gamma, dev), beta=T(beta, dev), out_scale=2.0)
+    assert torch.equal(y, y2)
+    nra.bn_train_forward(xt, xt, gamma=T(gamma, dev), beta=T(beta, dev), out_scale=2.0)  # in place
+    assert torch.equal(xt, y)
+
+
+# ------------------------------------------------------------------------------------------
+# Conv -> normalize -> epilogue
+# ------------------------------------------------------------------------------------------
+def test_conv_bn_workload4_full(dev, nra, orc):
+    import torch
+
+    inp = synth.host_inputs(4)
+    t = lambda a: T(a, dev)
+    args = (t(inp["x"]), t(inp["w"]), t(inp["b"]))
+    kw = dict(norm=nra.NR_NORM_BATCH_TRAIN, eps=inp["eps"], gamma=t(inp["gamma"]),
+              beta=t(inp["beta"]), out_scale=inp["scale"])
+    out = nra.conv_norm_epilogue_forward(*args, **kw)
+    ref = orc.conv_norm_epilogue(inp["x"], inp["w"], inp["b"], batch=True, gamma=inp["gamma"],
+                                 beta=inp["beta"], out_scale=inp["scale"])
+    err = maxerr(H(out), ref)
+    _log("conv2d(8->64) + bn_train + x2 on x[128,8,64,64]: max_abs_err %.3e" % err)
+    assert err <= TOL
+    assert torch.equal(out, nra.conv_norm_epilogue_forward(*args, **kw))
+
+
+def test_conv_in3d_workload5_full(dev, nra, orc):
+    import torch
+
+    inp = synth.host_inputs(5)
+    t = lambda a: T(a, dev)
+    args = (t(inp["x"]), t(inp["w"]), t(inp["b"]))
+    kw = dict(norm=nra.NR_NORM_INSTANCE, eps=inp["eps"], pre_mul=t(inp["mult"]),
+              clamp=inp["clamp"], post_mul=t(inp["mult"]), reduce_max_c=True)
+    out = nra.conv_norm_epilogue_forward(*args, **kw)
+    ref = orc.conv_norm_epilogue(inp["x"], inp["w"], inp["b"], batch=False, pre_mul=inp["mult"],
+                                 clamp=inp["clamp"], post_mul=inp["mult"], reduce_max_c=True)
+    err = maxerr(H(out), ref)
+    _log("conv3d(3->16) + IN3d + clamp + max_c on x[128,3,16,32,32]: max_abs_err %.3e" % err)
+    assert out.shape == (128, 14, 30, 30)
+    assert err <= TOL
+    assert torch.equal(out, nra.conv_norm_epilogue_forward(*args, **kw))
+
+
+CHAIN_CASES = [
+    # (x shape, Cout, batch, reduce_max_c, use every optional parameter)
+    ((2, 3, 9, 11), 5, True, False, True),
+    ((2, 3, 9, 11), 5, False, True, True),
+    ((3, 1, 5, 6, 7), 20, False, False, True),
+    ((3, 1, 5, 6, 7), 20, True, True, True),
+    ((1, 4, 3, 3), 16, True, False, False),
+    ((4, 2, 6, 7, 9), 17, False, True, False),
+    ((2, 8, 34, 35), 64, True, False, True),
+]
+
+
+@pytest.mark.parametrize("shape,cout,batch,red,full", CHAIN_CASES)
+def test_conv_chain_general(dev, nra, orc, shape, cout, batch, red, full):
+    g = np.random.Generator(np.random.PCG64(len(shape) * 100 + cout))
+    x = g.standard_normal(shape).astype(np.float32)
+    dims = len(shape) - 2
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32) if full else None
+    opt = lambda a: a if full else None
+    pm = opt(g.standard_normal(cout).astype(np.float32))
+    gm = opt(g.uniform(0.5, 1.5, cout).astype(np.float32))
+    bt = opt(g.uniform(-0.5, 0.5, cout).astype(np.float32))
+    qm = opt(g.standard_normal(cout).astype(np.float32))
+    clamp = (-0.8, 1.1) if full else None
+    t = lambda a: None if a is None else T(a, dev)
+    out = nra.conv_norm_epilogue_forward(
+        t(x), t(w), t(b), norm=nra.NR_NORM_BATCH_TRAIN if batch else nra.NR_NORM_INSTANCE,
+        pre_mul=t(pm), gamma=t(gm), beta=t(bt), out_scale=1.5 if full else 1.0, clamp=clamp,
+        post_mul=t(qm), reduce_max_c=red)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=batch, pre_mul=pm, gamma=gm, beta=bt,
+                                 out_scale=1.5 if full else 1.0, clamp=clamp, post_mul=qm,
+                                 reduce_max_c=red)
+    err = maxerr(H(out), ref)
+    _log("chain %s Cout %d batch %s max_c %s: max_abs_err %.3e" % (shape, cout, batch, red, err))
+    assert err <= TOL
+
+
+def test_stream_copy(dev, nra):
+    import torch
+
+    a = torch.randn(1 << 20, device=dev)
+    b = torch.empty_like(a)
+    nra.stream_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    c = torch.randn(1001, device=dev)
+    d = torch.empty_like(c)
+    nra.stream_copy(c, d)
+    torch.cuda.synchronize()
+    assert torch.equal(c, d)
