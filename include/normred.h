@@ -20,10 +20,12 @@
  *     surface at the caller's next synchronization, as with any HIP launch.
  *   - Results are deterministic: the same inputs and shapes give bit-identical outputs on
  *     every run (fixed reduction order; no floating-point atomics).
- *   - Workspace: a device buffer of at least the size the matching *_workspace_size query
- *     returns. It must be zero-filled once before its first use (nr_workspace_clear, or
- *     hipMemset); every call leaves it valid for the next call. Calls that share a workspace
- *     must be ordered (same stream, or synchronized): concurrent calls on one workspace race.
+ *   - Workspace: a device buffer (256-byte aligned) of at least the size the matching
+ *     *_workspace_size query returns. Its contents need no initialization and carry nothing
+ *     from one call to the next, except the sticky error word that nr_workspace_check reads
+ *     (zero the buffer once, e.g. with nr_workspace_clear, to use that check). Calls that share
+ *     a workspace must be ordered (same stream, or synchronized): concurrent calls on one
+ *     workspace race.
  */
 #ifndef NORMRED_H
 #define NORMRED_H

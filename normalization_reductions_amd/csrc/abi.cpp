@@ -146,7 +146,7 @@ bool may_need_exchange(int64_t S)
 }
 
 struct InormLayout {
-    size_t counters = 0, slots = 0, partials = 0, stats = 0, bytes = 0;
+    size_t slots = 0, partials = 0, stats = 0, bytes = 0;
     bool exchange = false;
     SplitGeom sg;
 };
@@ -158,10 +158,8 @@ InormLayout inorm_layout(int64_t N, int64_t C, int64_t S, bool vec)
     size_t off = kHeaderBytes;
     L.exchange = may_need_exchange(S);
     if (L.exchange) {
-        L.counters = off;
-        off = align_up(off + (size_t)slices * kCounterStride, kWsAlign);
         L.slots = off;
-        off = align_up(off + (size_t)slices * kMaxParts * 2 * sizeof(unsigned long long), kWsAlign);
+        off = align_up(off + resident_slot_bytes(slices, kMaxParts), kWsAlign);
     }
     L.sg = split_geometry(N, C, S, false, vec);
     L.partials = off;
@@ -364,7 +362,6 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
         a.beta = beta;
         a.save_mean = save_mean;
         a.save_invstd = save_invstd;
-        a.counters = L.exchange ? ws_at<uint32_t>(workspace, L.counters) : nullptr;
         a.slots = L.exchange ? ws_at<unsigned long long>(workspace, L.slots) : nullptr;
         a.flags = ws_at<uint32_t>(workspace, 0);
         if (C > 0x7fffffff) return fail(NR_ERR_UNSUPPORTED, "%s: C too large for the resident variant", fn);

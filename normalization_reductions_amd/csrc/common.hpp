@@ -83,14 +83,14 @@ __device__ __forceinline__ void st_stream(f4* p, f4 v) { __builtin_nontemporal_s
 __device__ __forceinline__ float ld_stream1(const float* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream1(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
-// Exchange words between co-resident workgroups: 64-bit, tagged with an epoch in the high
-// half and an fp32 payload in the low half. They are only ever accessed with relaxed
-// agent-scope atomics, so each word is read whole and coherently across the XCDs' L2s;
-// a reader accepts a word only when its tag equals the epoch it waits for.
-__device__ __forceinline__ void xchg_store(unsigned long long* p, uint32_t epoch, float v)
+// Exchange words between co-resident workgroups: 64-bit, a tag in the high half and an fp32
+// payload in the low half. They are only ever accessed with relaxed agent-scope atomics, so
+// each word is read whole and coherently across the XCDs' L2s; a reader accepts a word only
+// when its tag says it was written by the current launch.
+__device__ __forceinline__ void xchg_store(unsigned long long* p, uint32_t tag, float v)
 {
     const unsigned long long w =
-        ((unsigned long long)epoch << 32) | (unsigned long long)__float_as_uint(v);
+        ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(v);
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -99,9 +99,10 @@ __device__ __forceinline__ unsigned long long xchg_load(unsigned long long* p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Upper bound on polling rounds in a co-residency wait; with ~1 us of sleep per round this is
-// far beyond any legitimate wait (all waiters are co-resident by construction), and it keeps
-// a broken launch from spinning forever: the wait gives up and raises a sticky flag.
+// Upper bound on polling rounds in a co-residency wait. A round is a short sleep plus two
+// device-coherent loads, so 2^22 rounds is far beyond any legitimate wait (every waiter's
+// siblings are co-resident by construction); it keeps a broken launch from spinning forever:
+// the wait gives up and raises a sticky flag.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kFlagSpinTimeout = 1u;
 

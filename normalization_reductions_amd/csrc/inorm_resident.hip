@@ -5,19 +5,21 @@
 //
 // Design (MI355X-first; the page's own kernel reads each slice twice -- a Welford pass and a
 // normalize pass -- which caps a bandwidth-bound kernel at two thirds of the HBM roofline):
-//   * A slice is split into P parts (P = 1, 2, 4, 8 or 16). One workgroup owns one part and
+//   * A slice is split into P parts (1 <= P <= 16). One workgroup owns one part and
 //     keeps it in VGPRs from load to store, so x crosses HBM exactly once and y once.
 //   * Per thread: 16-byte non-temporal loads, statistics of its own values by the two-pass
 //     formula over registers, relative to a per-slice pivot K = x[slice][0] (removes the
 //     offset before any sum: the cancellation the page's numerics discussion worries about).
 //   * Wave64 butterfly Chan merges, then an LDS combine across the workgroup's waves.
 //   * P > 1: the P workgroups of a slice are co-resident (cooperative launch of a persistent
-//     grid, units dealt round-robin so the P parts of a slice run in the same round). Each
-//     publishes (mean, M2) as two epoch-tagged 64-bit words with relaxed agent-scope atomic
-//     stores and polls its siblings' words the same way; no cache-wide fences are needed
-//     because every exchanged word carries its own validity tag. The P partials are merged in
-//     part order 0..P-1 by every sibling, so all parts normalize with identical statistics and
-//     the result does not depend on arrival order.
+//     grid whose size is a multiple of P; units are dealt so that the same P consecutive
+//     workgroups own the P parts of a slice in every round). Each publishes (mean, M2) as two
+//     tagged 64-bit words with relaxed agent-scope atomic stores and polls its siblings' words
+//     the same way. The slot region is zero-filled just before the launch, so a non-zero tag
+//     marks a word written by this launch; because every exchanged word carries its own
+//     validity tag, no cache-wide release/acquire fences are needed. The P partials are merged
+//     in part order 0..P-1 by every sibling, so all parts normalize with identical statistics
+//     and the result does not depend on arrival order.
 //   * Normalize from registers: y = ((x - K) - mean_d) * (rstd * gamma) + beta, 16-byte
 //     non-temporal stores.
 #include "common.hpp"
@@ -26,9 +28,8 @@
 namespace nr {
 namespace {
 
-// Counter increment per part: P parts together add kEpochStep per slice per launch, for every
-// P in 1..16 (kEpochStep is divisible by each of them), so a slice's epoch is counter/step.
-constexpr unsigned long long kEpochStep = 720720ull;  // lcm(1..16)
+// Tag of an exchange word written by the current launch (the slots start zeroed).
+constexpr uint32_t kTag = 1u;
 
 template <int BLOCK, int VEC, int WAVES_PER_EU>
 __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK, BLOCK),
@@ -129,18 +130,10 @@ inorm_resident_kernel(ResidentArgs a)
             w = wave_merge<NW>(w);  // lanes 0..NW-1: this part's statistics
 
             if (P > 1) {
-                unsigned long long* cntp = reinterpret_cast<unsigned long long*>(
-                    reinterpret_cast<char*>(a.counters) + slice * kCounterStride);
-                unsigned long long old = 0;
-                if (lane == 0)
-                    old = __hip_atomic_fetch_add(cntp, kEpochStep / (unsigned long long)P,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t epoch = (uint32_t)(
-                    __builtin_amdgcn_readfirstlane((uint32_t)(old / kEpochStep)) + 1u);
-                unsigned long long* sl = a.slots + (size_t)slice * kMaxParts * 2;
+                unsigned long long* sl = a.slots + (size_t)slice * P * 2;
                 if (lane == 0) {
-                    xchg_store(sl + part * 2 + 0, epoch, w.mean);
-                    xchg_store(sl + part * 2 + 1, epoch, w.m2);
+                    xchg_store(sl + part * 2 + 0, kTag, w.mean);
+                    xchg_store(sl + part * 2 + 1, kTag, w.m2);
                 }
                 Stat ps = stat_empty();
                 if (lane < P) {
@@ -149,7 +142,7 @@ inorm_resident_kernel(ResidentArgs a)
                     for (;;) {
                         w0 = xchg_load(sl + lane * 2 + 0);
                         w1 = xchg_load(sl + lane * 2 + 1);
-                        if ((uint32_t)(w0 >> 32) == epoch && (uint32_t)(w1 >> 32) == epoch) break;
+                        if ((uint32_t)(w0 >> 32) == kTag && (uint32_t)(w1 >> 32) == kTag) break;
                         if (++spins > kSpinLimit) {
                             raise_flag(a.flags, kFlagSpinTimeout);
                             break;
@@ -252,6 +245,8 @@ hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStr
     if (grid > units) grid = units;
     grid -= grid % a.P;  // every round holds whole slices
     if (grid < a.P) return hipErrorCooperativeLaunchTooLarge;
+    const hipError_t e = launch_fill_zero(a.slots, resident_slot_bytes(a.slices, a.P), stream);
+    if (e != hipSuccess) return e;
     return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(cfg.block), params, 0, stream);
 }
 

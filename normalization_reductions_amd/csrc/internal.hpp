@@ -14,7 +14,6 @@ namespace nr {
 constexpr size_t kWsAlign = 256;
 constexpr size_t kHeaderBytes = 256;     // uint32 flags at offset 0
 constexpr int kMaxParts = 16;            // parts per slice in the co-resident variant
-constexpr size_t kCounterStride = 128;   // bytes per slice epoch counter (one cache line)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -44,10 +43,15 @@ struct ResidentArgs {
     const float* beta;
     float* save_mean;
     float* save_invstd;
-    uint32_t* counters;          // [slices] epoch counters, kCounterStride apart
-    unsigned long long* slots;   // [slices][kMaxParts][2] tagged exchange words
+    unsigned long long* slots;   // [slices][P][2] tagged exchange words (zero-filled per launch)
     uint32_t* flags;             // sticky error word
 };
+
+// Bytes of exchange slots a launch with P parts uses (zero-filled by launch_resident).
+inline size_t resident_slot_bytes(int64_t slices, int P)
+{
+    return P > 1 ? (size_t)slices * (size_t)P * 2 * sizeof(unsigned long long) : 0;
+}
 
 // Largest grid the kernel can have fully co-resident (0 if the configuration is unknown).
 int resident_max_grid(const ResidentCfg& cfg);

@@ -190,14 +190,44 @@ EDGE_SHAPES = [(1, 1, 1), (3, 2, 5), (2, 3, 1023), (1, 1, 4), (2, 2, 65540), (1,
                (4, 2, 100000), (1, 1, 1048576), (2, 1, 1048580), (5, 7, 12600), (1, 1, 7)]
 
 
+@pytest.fixture(scope="module")
+def shared_ws(dev):
+    """One workspace reused by calls of every shape and variant (sized for the largest)."""
+    import torch
+
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    return ws
+
+
 @pytest.mark.parametrize("shape", EDGE_SHAPES)
 @pytest.mark.parametrize("variant", [0, 2])
-def test_inorm_edge_shapes(dev, nra, orc, shape, variant):
+def test_inorm_edge_shapes(dev, nra, orc, shared_ws, shape, variant):
     x = synth.per_slice_affine_normal(shape, 7 + shape[2], (0.1, 10.0), (-100.0, 100.0))
-    y = nra.inorm_forward(T(x, dev), variant=variant)
+    y = nra.inorm_forward(T(x, dev), variant=variant, workspace=shared_ws)
     err = maxerr(H(y), orc.instance_norm(x))
     _log("inorm edge %s variant %d: max_abs_err %.3e" % (shape, variant, err))
     assert err <= TOL
+    assert nra.workspace_check(shared_ws) == 0
+
+
+def test_inorm_workspace_carries_no_state(dev, nra, orc):
+    # A workspace full of arbitrary bytes, reused across shapes whose regions overlap
+    # differently (split partials over the exchange slots of another shape, 3 then 9 then 2
+    # parts), must not change any result.
+    import torch
+
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device=dev)
+    ws[:256] = 0  # the sticky error word is the one thing read across calls
+    seq = [((2, 2, 65540), 0), ((3, 2, 5), 2), ((1, 3, 262148), 0), ((2, 3, 1023), 2),
+           ((1, 3, 262148), 0), ((16, 4, 65536), 0), ((2, 2, 65540), 2), ((1, 3, 262148), 1)]
+    for i, (shape, variant) in enumerate(seq):
+        x = synth.per_slice_affine_normal(shape, 300 + i, (0.1, 10.0), (-100.0, 100.0))
+        y = nra.inorm_forward(T(x, dev), variant=variant, workspace=ws)
+        err = maxerr(H(y), orc.instance_norm(x))
+        _log("shared dirty workspace step %d %s variant %d: max_abs_err %.3e"
+             % (i, shape, variant, err))
+        assert err <= TOL
+        assert nra.workspace_check(ws) == 0
 
 
 def test_inorm_empty_batch(dev, nra):
