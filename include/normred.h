@@ -65,7 +65,8 @@ const char* nr_version(void);
  * x, y       : [N, C, S] fp32 device buffers. y may equal x (in place); partial overlap is
  *              rejected (NR_ERR_INVALID_ARG).
  * N, C, S    : sizes; S >= 1, N >= 0, C >= 0. N*C == 0 is an empty batch: NR_OK, nothing
- *              enqueued (workspace may then be NULL). N*C*S*4 must fit in int64.
+ *              enqueued, and every pointer (x, y, workspace, ...) may be NULL. N*C*S*4 must
+ *              fit in int64.
  * eps        : added to the variance inside the square root (the pages use 1e-5); >= 0.
  * gamma,beta : [C] device buffers, or both NULL (affine = False). One without the other is
  *              rejected.
@@ -104,7 +105,7 @@ nr_status inorm_forward_ex(const float* x, float* y, int64_t N, int64_t C, int64
  *
  * x, y       : [N, C, S] fp32 device buffers; y may equal x.
  * N, C, S    : N >= 1 and S >= 1 (statistics over nothing are undefined); C >= 0 (C == 0 is
- *              a no-op).
+ *              a no-op that accepts NULL pointers).
  * gamma,beta : [C] device buffers, or both NULL (identity affine).
  * out_scale  : final multiplier (1.0f for plain batch norm).
  * save_mean, save_invstd : [C] device outputs, or NULL.
@@ -137,7 +138,7 @@ nr_status bn_train_forward(const float* x, float* y, int64_t N, int64_t C, int64
  * Shapes: x [N, C_in, (D,) H, W]; w [C_out, C_in, (3,) 3, 3]; b [C_out] or NULL;
  * out [N, (D-2,) H-2, W-2] if reduce_max_c else [N, C_out, (D-2,) H-2, W-2].
  * spatial_dims is 2 (D ignored) or 3. Every optional [C_out] pointer may be NULL. N == 0 is an
- * empty batch (NR_OK, nothing enqueued).
+ * empty batch (NR_OK, nothing enqueued; x, w, out and workspace may be NULL).
  * ------------------------------------------------------------------------------------------ */
 #define NR_NORM_BATCH_TRAIN 1
 #define NR_NORM_INSTANCE 2

@@ -311,10 +311,13 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
     size_t workspace_bytes, int variant, hipStream_t stream)
 {
     static const char* fn = "inorm_forward";
-    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
     int64_t total = 0;
     nr_status s = check_sizes(N, C, S, &total, fn);
     if (s != NR_OK) return s;
+    if (variant != NR_VARIANT_AUTO && variant != NR_VARIANT_RESIDENT && variant != NR_VARIANT_SPLIT)
+        return fail(NR_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (total == 0) return NR_OK;  // empty batch: nothing is read or written
+    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
     if (!aligned(x, 4) || !aligned(y, 4)) return fail(NR_ERR_MISALIGNED, "%s: x and y must be 4-byte aligned", fn);
     if (ranges_partially_overlap(x, y, total))
         return fail(NR_ERR_INVALID_ARG, "%s: x and y overlap without being the same buffer", fn);
@@ -325,9 +328,6 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
     if ((s = check_opt(beta, "beta", fn)) != NR_OK) return s;
     if ((s = check_opt(save_mean, "save_mean", fn)) != NR_OK) return s;
     if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
-    if (variant != NR_VARIANT_AUTO && variant != NR_VARIANT_RESIDENT && variant != NR_VARIANT_SPLIT)
-        return fail(NR_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
-    if (total == 0) return NR_OK;  // empty batch: nothing to do
 
     const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
     const InormLayout L = inorm_layout(N, C, S, vec);
@@ -398,11 +398,12 @@ __attribute__((visibility("default"))) nr_status bn_train_forward(
     size_t workspace_bytes, hipStream_t stream)
 {
     static const char* fn = "bn_train_forward";
-    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
     if (N < 1) return fail(NR_ERR_INVALID_ARG, "%s: batch statistics need N >= 1", fn);
     int64_t total = 0;
     nr_status s = check_sizes(N, C, S, &total, fn);
     if (s != NR_OK) return s;
+    if (total == 0) return NR_OK;  // no channels: nothing is read or written
+    if (!x || !y) return fail(NR_ERR_INVALID_ARG, "%s: x and y must be non-NULL", fn);
     if (!aligned(x, 4) || !aligned(y, 4)) return fail(NR_ERR_MISALIGNED, "%s: x and y must be 4-byte aligned", fn);
     if (ranges_partially_overlap(x, y, total))
         return fail(NR_ERR_INVALID_ARG, "%s: x and y overlap without being the same buffer", fn);
@@ -414,7 +415,6 @@ __attribute__((visibility("default"))) nr_status bn_train_forward(
     if ((s = check_opt(beta, "beta", fn)) != NR_OK) return s;
     if ((s = check_opt(save_mean, "save_mean", fn)) != NR_OK) return s;
     if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
-    if (total == 0) return NR_OK;  // no channels
     const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
     SplitGeom g;
     size_t off_p, off_s;
@@ -439,8 +439,8 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     ConvGeom g;
     nr_status s = check_desc(d, &g, fn);
     if (s != NR_OK) return s;
+    if (g.N == 0) return NR_OK;  // empty batch: nothing is read or written
     if (!x || !w || !out) return fail(NR_ERR_INVALID_ARG, "%s: x, w and out must be non-NULL", fn);
-    if (g.N == 0) return NR_OK;  // empty batch
     if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (b && !aligned(b, 4)))
         return fail(NR_ERR_MISALIGNED, "%s: tensors must be 4-byte aligned", fn);
     const bool batch = d->norm == NR_NORM_BATCH_TRAIN;

@@ -94,6 +94,8 @@ def test_inorm_rejects(lib, kw, status):
 
 def test_empty_batches_are_noops_without_workspace(lib):
     assert lib.inorm_forward(FAKE, FAKE, 0, 5, 16, 1e-5, None, None, None, None, None, 0, None) == 0
+    assert lib.inorm_forward(None, None, 0, 5, 16, 1e-5, None, None, None, None, None, 0, None) == 0
+    assert lib.inorm_forward(None, None, 0, 5, 0, 1e-5, None, None, None, None, None, 0, None) == 1
     assert lib.inorm_forward(FAKE, FAKE, 3, 0, 16, 1e-5, None, None, None, None, None, 0, None) == 0
     assert lib.bn_train_forward(FAKE, FAKE, 2, 0, 4, 1e-5, None, None, 1.0, None, None, None, 0,
                                 None) == 0
