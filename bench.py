@@ -233,8 +233,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "inorm_resident_kernel<512,16> (read-once, 8 parts/slice)"
-                               if args.variant != "split" else "split partial/merge/apply"},
+                     "kernel": "inorm_pipelined_kernel<256,16> (read-once, 16 parts of 64 KiB "
+                               "per slice)" if args.variant != "split"
+                               else "split partial/merge/apply"},
         "cpu_baseline": None,
     }
     if not args.no_extra:

@@ -95,54 +95,40 @@ bool resident_override(int* block, int* vec)
 }
 
 // Pick the resident configuration and part count for slice length S (S % 4 == 0 required).
+// Without an override: slices that fit one 256-thread workgroup (<= 16K elements) take the
+// smallest single-workgroup configuration; larger slices take the pipelined kernel with
+// 64 KiB parts (256 threads x 16 float4), or 128 KiB parts past 32 of those.
 bool choose_resident(int64_t S, int* cfg_idx, int* P)
 {
     if (S % 4 != 0) return false;
     const int n = resident_cfg_count();
     int ob, ov;
-    if (resident_override(&ob, &ov)) {
-        for (int i = 0; i < n; ++i) {
-            const ResidentCfg c = resident_cfg(i);
-            if (c.block == ob && c.vec == ov) {
-                const int64_t p = (S + c.part_len - 1) / c.part_len;
-                if (p > kMaxParts) return false;
-                *cfg_idx = i;
-                *P = (int)p;
-                return true;
-            }
-        }
-        return false;
-    }
-    // Slices up to 16K elements: one workgroup, the smallest configuration that holds it.
+    const bool over = resident_override(&ob, &ov);
     for (int i = 0; i < n; ++i) {
         const ResidentCfg c = resident_cfg(i);
-        if (c.part_len >= S && c.block == 256) {
-            *cfg_idx = i;
-            *P = 1;
-            return true;
-        }
-    }
-    // Larger slices: 512-thread parts of 32K elements (two workgroups share a CU), then
-    // 1024-thread parts of 64K elements.
-    for (int i = 0; i < n; ++i) {
-        const ResidentCfg c = resident_cfg(i);
-        if (c.block < 512) continue;
+        if (over && (c.block != ob || c.vec != ov)) continue;
         const int64_t p = (S + c.part_len - 1) / c.part_len;
-        if (p <= kMaxParts) {
-            *cfg_idx = i;
-            *P = (int)p;
-            return true;
+        if (!c.pipelined) {
+            if (p != 1 || (!over && c.block != 256)) continue;
+        } else {
+            if (p < 2 || p > kMaxParts) continue;
+            if (!over && c.vec != 16) continue;
         }
+        *cfg_idx = i;
+        *P = (int)p;
+        return true;
     }
     return false;
 }
 
-// Could any resident configuration (including an override) need the exchange regions?
+// Could a resident configuration (including an override) need the exchange regions?
 bool may_need_exchange(int64_t S)
 {
     if (S % 4 != 0 || S <= 1024) return false;
-    const ResidentCfg big = resident_cfg(resident_cfg_count() - 1);
-    return S <= (int64_t)kMaxParts * big.part_len;
+    int64_t biggest = 0;
+    for (int i = 0; i < resident_cfg_count(); ++i)
+        if (resident_cfg(i).pipelined && resident_cfg(i).part_len > biggest) biggest = resident_cfg(i).part_len;
+    return S <= (int64_t)kMaxParts * biggest;
 }
 
 struct InormLayout {
@@ -158,8 +144,8 @@ InormLayout inorm_layout(int64_t N, int64_t C, int64_t S, bool vec)
     size_t off = kHeaderBytes;
     L.exchange = may_need_exchange(S);
     if (L.exchange) {
-        L.slots = off;
-        off = align_up(off + resident_slot_bytes(slices, kMaxParts), kWsAlign);
+        L.slots = off;  // counter, then slots
+        off = align_up(off + resident_ws_bytes(slices, kMaxParts), kWsAlign);
     }
     L.sg = split_geometry(N, C, S, false, vec);
     L.partials = off;
@@ -362,9 +348,11 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
         a.beta = beta;
         a.save_mean = save_mean;
         a.save_invstd = save_invstd;
-        a.slots = L.exchange ? ws_at<unsigned long long>(workspace, L.slots) : nullptr;
+        a.counter = L.exchange ? ws_at<uint32_t>(workspace, L.slots) : nullptr;
+        a.slots = L.exchange ? ws_at<unsigned long long>(workspace, L.slots + kCounterBytes) : nullptr;
         a.flags = ws_at<uint32_t>(workspace, 0);
-        if (C > 0x7fffffff) return fail(NR_ERR_UNSUPPORTED, "%s: C too large for the resident variant", fn);
+        if (C > 0x7fffffff || a.slices * P > 0xF0000000LL)  // counter headroom for final grabs
+            return fail(NR_ERR_UNSUPPORTED, "%s: too many slices for the resident variant", fn);
         const hipError_t e = launch_resident(cfg, a, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;

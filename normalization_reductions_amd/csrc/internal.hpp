@@ -13,7 +13,7 @@ namespace nr {
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kWsAlign = 256;
 constexpr size_t kHeaderBytes = 256;     // uint32 flags at offset 0
-constexpr int kMaxParts = 16;            // parts per slice in the co-resident variant
+constexpr int kMaxParts = 32;            // parts per slice in the co-resident variant
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -22,9 +22,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // holding its part in registers.
 // ---------------------------------------------------------------------------------------------
 struct ResidentCfg {
-    int block;     // threads per workgroup
-    int vec;       // float4 registers per thread
-    int part_len;  // elements per part = block * 4 * vec
+    int block;       // threads per workgroup
+    int vec;         // float4 registers per thread (per buffer)
+    int part_len;    // elements per part = block * 4 * vec
+    bool pipelined;  // false: one workgroup per slice (P == 1); true: persistent, P > 1
 };
 
 // The configurations compiled into the library, ascending by part length.
@@ -43,14 +44,17 @@ struct ResidentArgs {
     const float* beta;
     float* save_mean;
     float* save_invstd;
-    unsigned long long* slots;   // [slices][P][2] tagged exchange words (zero-filled per launch)
+    uint32_t* counter;           // next unit to take; followed (256 B on) by the slots
+    unsigned long long* slots;   // [slices][P][2] tagged exchange words
     uint32_t* flags;             // sticky error word
 };
 
-// Bytes of exchange slots a launch with P parts uses (zero-filled by launch_resident).
-inline size_t resident_slot_bytes(int64_t slices, int P)
+// Bytes a launch with P parts uses at `counter` (counter, then slots), zero-filled by
+// launch_resident before every launch.
+constexpr size_t kCounterBytes = 256;
+inline size_t resident_ws_bytes(int64_t slices, int P)
 {
-    return P > 1 ? (size_t)slices * (size_t)P * 2 * sizeof(unsigned long long) : 0;
+    return P > 1 ? kCounterBytes + (size_t)slices * (size_t)P * 2 * sizeof(unsigned long long) : 0;
 }
 
 // Largest grid the kernel can have fully co-resident (0 if the configuration is unknown).

@@ -157,14 +157,15 @@ def test_inorm_workload3_full_size(dev, nra, orc, w3, variant):
 # Instance norm: every compiled read-once configuration, ragged parts, edge shapes
 # ------------------------------------------------------------------------------------------
 RESIDENT_CASES = [
-    # (block, vec, S): P = ceil(S / (block*4*vec)) covers 1, ragged 3, and the 16-part maximum
-    (256, 1, 1024), (256, 1, 3000), (256, 1, 16384),
-    (256, 2, 2048), (256, 2, 6148),
-    (256, 4, 4096), (256, 4, 40960),
-    (256, 8, 8192), (256, 8, 20000),
-    (256, 16, 16384), (256, 16, 12600), (256, 16, 40000),
-    (512, 16, 32768), (512, 16, 262144), (512, 16, 65540), (512, 16, 524288),
-    (1024, 16, 65536), (1024, 16, 1048576), (1024, 16, 200004),
+    # (block, vec, S). S <= block*4*vec: one workgroup per slice (full and ragged);
+    # larger S: the pipelined kernel with P = ceil(S / (block*4*vec)) parts -- 2, ragged,
+    # a 4-element last part, and the 32-part maximum.
+    (256, 1, 1024), (256, 1, 1000), (256, 2, 2048), (256, 4, 4096), (256, 8, 8192),
+    (256, 16, 16384), (256, 16, 12600), (512, 16, 32768), (512, 16, 20000),
+    (1024, 16, 65536), (1024, 16, 50000),
+    (256, 8, 16384), (256, 8, 20000), (256, 8, 262144),
+    (256, 16, 262144), (256, 16, 65540), (256, 16, 524288), (256, 16, 40000),
+    (512, 16, 65536), (512, 16, 1048576), (512, 16, 200004),
 ]
 
 
