@@ -33,7 +33,7 @@ N, C, H, W = 112, 64, 512, 512
 S = H * W
 MIN_BYTES = 2 * 4 * N * C * S
 METRIC = "InstanceNorm2d fp32 effective GB/s (min bytes/time) and % of HBM peak, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "inorm_resident_112x64x512x512_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "inorm_pipelined_112x64x512x512_traffic.json")
 KERNEL_SOURCES = ["normalization_reductions_amd/csrc/inorm_resident.hip",
                   "normalization_reductions_amd/csrc/common.hpp",
                   "normalization_reductions_amd/csrc/internal.hpp"]

@@ -21,24 +21,19 @@ __global__ __launch_bounds__(kBlock) void fill_zero_bytes_kernel(unsigned char* 
     if (i < n) p[i] = 0;
 }
 
-// Each thread moves 4 x 16 bytes per iteration; the grid strides over the whole buffer.
+// One 16-byte vector per thread, one 4 KiB chunk per workgroup, a one-shot grid. Workgroups
+// are dealt to the XCDs round-robin, so chunk b is remapped to let each XCD stream its own
+// contiguous eighth of the buffer (measured the fastest copy pattern on MI355X: a fine-grained
+// stream per XCD beats persistent grids and large per-workgroup chunks).
 __global__ __launch_bounds__(kBlock) void copy_vec_kernel(const f4* __restrict__ s,
-                                                          f4* __restrict__ d, int64_t nv)
+                                                          f4* __restrict__ d, int64_t nv,
+                                                          int64_t nchunks)
 {
-    const int64_t stride = (int64_t)gridDim.x * kBlock * 4;
-    for (int64_t i0 = (int64_t)blockIdx.x * kBlock * 4 + threadIdx.x; i0 < nv; i0 += stride) {
-        f4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t i = i0 + j * kBlock;
-            if (i < nv) v[j] = ld_stream(s + i);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t i = i0 + j * kBlock;
-            if (i < nv) st_stream(d + i, v[j]);
-        }
-    }
+    int64_t b = blockIdx.x;
+    const int64_t n8 = nchunks / 8 * 8;
+    if (b < n8) b = (b % 8) * (n8 / 8) + b / 8;
+    const int64_t i = b * kBlock + threadIdx.x;
+    if (i < nv) st_stream(d + i, ld_stream(s + i));
 }
 
 __global__ __launch_bounds__(kBlock) void copy_scalar_kernel(const float* __restrict__ s,
@@ -47,15 +42,6 @@ __global__ __launch_bounds__(kBlock) void copy_scalar_kernel(const float* __rest
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * kBlock)
         d[i] = s[i];
-}
-
-int cu_count()
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 256;
-    return cus > 0 ? cus : 256;
 }
 
 }  // namespace
@@ -81,13 +67,11 @@ hipError_t launch_stream_copy(const float* src, float* dst, int64_t n, hipStream
     if (n <= 0) return hipSuccess;
     const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0 &&
                      (n & 3) == 0;
-    if (vec) {
+    if (vec && (n / 4 + kBlock - 1) / kBlock <= 0x7fffffffLL) {
         const int64_t nv = n / 4;
-        int64_t grid = (nv + kBlock * 4 - 1) / (kBlock * 4);
-        const int64_t cap = (int64_t)cu_count() * 8;  // a few resident waves per SIMD, persistent
-        if (grid > cap) grid = cap;
-        copy_vec_kernel<<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(
-            reinterpret_cast<const f4*>(src), reinterpret_cast<f4*>(dst), nv);
+        const int64_t nchunks = (nv + kBlock - 1) / kBlock;
+        copy_vec_kernel<<<dim3((unsigned)nchunks), dim3(kBlock), 0, stream>>>(
+            reinterpret_cast<const f4*>(src), reinterpret_cast<f4*>(dst), nv, nchunks);
     } else {
         int64_t grid = (n + kBlock - 1) / kBlock;
         if (grid > 65536) grid = 65536;
