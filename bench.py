@@ -34,9 +34,9 @@ S = H * W
 MIN_BYTES = 2 * 4 * N * C * S
 METRIC = "InstanceNorm2d fp32 effective GB/s (min bytes/time) and % of HBM peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "inorm_pipelined_112x64x512x512_traffic.json")
-KERNEL_SOURCES = ["normalization_reductions_amd/csrc/inorm_resident.hip",
-                  "normalization_reductions_amd/csrc/common.hpp",
-                  "normalization_reductions_amd/csrc/internal.hpp"]
+KERNEL_SOURCES = ["normalization_reductions_amd/csrc/resident_norm.hip",
+                  "normalization_reductions_amd/csrc/resident.hpp",
+                  "normalization_reductions_amd/csrc/common.hpp"]
 
 
 def log(msg):
@@ -233,7 +233,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "inorm_pipelined_kernel<256,16> (read-once, 16 parts of 64 KiB "
+                     "kernel": "norm_pipelined_kernel<256,16> (read-once, 16 parts of 64 KiB "
                                "per slice)" if args.variant != "split"
                                else "split partial/merge/apply"},
         "cpu_baseline": None,

@@ -139,6 +139,10 @@ nr_status bn_train_forward(const float* x, float* y, int64_t N, int64_t C, int64
  * out [N, (D-2,) H-2, W-2] if reduce_max_c else [N, C_out, (D-2,) H-2, W-2].
  * spatial_dims is 2 (D ignored) or 3. Every optional [C_out] pointer may be NULL. N == 0 is an
  * empty batch (NR_OK, nothing enqueued; x, w, out and workspace may be NULL).
+ * When reduce_max_c == 0 and the output's spatial size is a multiple of 4 (and the statistics
+ * groups fit the read-once kernels), the conv writes straight into `out`, which is then
+ * normalized in place: `out` must be 16-byte aligned (else NR_ERR_MISALIGNED) and the workspace
+ * holds only exchange slots. Otherwise the conv output is staged in the workspace.
  * ------------------------------------------------------------------------------------------ */
 #define NR_NORM_BATCH_TRAIN 1
 #define NR_NORM_INSTANCE 2

@@ -94,20 +94,22 @@ bool resident_override(int* block, int* vec)
     return false;
 }
 
-// Pick the resident configuration and part count for slice length S (S % 4 == 0 required).
-// Without an override: slices that fit one 256-thread workgroup (<= 16K elements) take the
-// smallest single-workgroup configuration; larger slices take the pipelined kernel with
-// 64 KiB parts (256 threads x 16 float4), or 128 KiB parts past 32 of those.
-bool choose_resident(int64_t S, int* cfg_idx, int* P)
+// Pick a read-once configuration and part count for groups of L values of the given kind.
+// Without an override: groups that fit one 256-thread workgroup (<= 16K values) take the
+// smallest single-workgroup configuration of the kind; larger groups take the pipelined
+// kernel with 64 KiB parts (256 threads x 16 float4), or 128 KiB parts past 32 of those.
+// Grouped kinds (batch norm) need L < 2^21 for their index arithmetic.
+bool choose_resident(int64_t L, bool grouped, bool chain, int* cfg_idx, int* P)
 {
-    if (S % 4 != 0) return false;
+    if (grouped && L >= (1 << 21)) return false;
     const int n = resident_cfg_count();
     int ob, ov;
     const bool over = resident_override(&ob, &ov);
     for (int i = 0; i < n; ++i) {
         const ResidentCfg c = resident_cfg(i);
+        if (c.grouped != grouped || c.chain != chain) continue;
         if (over && (c.block != ob || c.vec != ov)) continue;
-        const int64_t p = (S + c.part_len - 1) / c.part_len;
+        const int64_t p = (L + c.part_len - 1) / c.part_len;
         if (!c.pipelined) {
             if (p != 1 || (!over && c.block != 256)) continue;
         } else {
@@ -121,14 +123,43 @@ bool choose_resident(int64_t S, int* cfg_idx, int* P)
     return false;
 }
 
-// Could a resident configuration (including an override) need the exchange regions?
-bool may_need_exchange(int64_t S)
+// Could a read-once configuration of this kind need the exchange regions for groups of L?
+bool may_need_exchange(int64_t L, bool grouped)
 {
-    if (S % 4 != 0 || S <= 1024) return false;
+    if (L <= 1024 || (grouped && L >= (1 << 21))) return false;
     int64_t biggest = 0;
     for (int i = 0; i < resident_cfg_count(); ++i)
         if (resident_cfg(i).pipelined && resident_cfg(i).part_len > biggest) biggest = resident_cfg(i).part_len;
-    return S <= (int64_t)kMaxParts * biggest;
+    return L <= (int64_t)kMaxParts * biggest;
+}
+
+// Fill the fields of ResidentArgs that every kind shares.
+ResidentArgs resident_args(const float* x, float* y, int64_t N, int64_t C, int64_t S, bool batch,
+                           int P, float eps, const float* gamma, const float* beta,
+                           float out_scale, float* save_mean, float* save_invstd, void* ws,
+                           size_t exch_off, bool exch)
+{
+    ResidentArgs a{};
+    a.x = x;
+    a.y = y;
+    a.S = S;
+    a.C = C;
+    a.groups = batch ? C : N * C;
+    a.L = batch ? N * S : S;
+    a.div_magic = resident_div_magic(S);
+    a.batch = batch ? 1 : 0;
+    a.P = P;
+    a.eps = eps;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.out_scale = out_scale;
+    a.save_mean = save_mean;
+    a.save_invstd = save_invstd;
+    a.counter = exch ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + exch_off) : nullptr;
+    a.slots = exch ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + exch_off + kCounterBytes)
+                   : nullptr;
+    a.flags = reinterpret_cast<uint32_t*>(ws);
+    return a;
 }
 
 struct InormLayout {
@@ -142,7 +173,7 @@ InormLayout inorm_layout(int64_t N, int64_t C, int64_t S, bool vec)
     InormLayout L;
     const int64_t slices = N * C;
     size_t off = kHeaderBytes;
-    L.exchange = may_need_exchange(S);
+    L.exchange = S % 4 == 0 && may_need_exchange(S, false);
     if (L.exchange) {
         L.slots = off;  // counter, then slots
         off = align_up(off + resident_ws_bytes(slices, kMaxParts), kWsAlign);
@@ -187,10 +218,16 @@ nr_status run_split(const SplitGeom& g, const float* x, float* y, float eps, con
     return NR_OK;
 }
 
-size_t bn_layout(int64_t N, int64_t C, int64_t S, bool vec, SplitGeom* g, size_t* partials, size_t* stats)
+size_t bn_layout(int64_t N, int64_t C, int64_t S, bool vec, SplitGeom* g, size_t* exch,
+                 size_t* partials, size_t* stats)
 {
     *g = split_geometry(N, C, S, true, vec);
     size_t off = kHeaderBytes;
+    *exch = 0;
+    if (S % 4 == 0 && may_need_exchange(N * S, true)) {
+        *exch = off;
+        off = align_up(off + resident_ws_bytes(C, kMaxParts), kWsAlign);
+    }
     *partials = off;
     off = align_up(off + (size_t)(g->slices * g->chunks) * sizeof(float2), kWsAlign);
     *stats = off;
@@ -253,21 +290,38 @@ nr_status check_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
 }
 
 struct ChainLayout {
+    bool resident = false;  // normalize in place in `out` with a read-once kernel
+    int cfg_idx = -1, P = 0;
+    size_t exch = 0;
     size_t cbuf = 0, partials = 0, stats = 0, bytes = 0;
     SplitGeom sg;
 };
 
-ChainLayout chain_layout(const ConvGeom& g, bool batch)
+// Two plans. Without the max over channels and with S % 4 == 0 the conv writes its output
+// straight into `out` and a read-once kernel normalizes it in place (workspace: exchange slots
+// only). Otherwise the conv output goes to the workspace, statistics take the split path and
+// the chain epilogue writes `out`.
+ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
 {
     ChainLayout L;
     size_t off = kHeaderBytes;
+    const int64_t groups = batch ? g.Cout : g.N * g.Cout;
+    const int64_t len = batch ? g.N * g.SP : g.SP;
+    if (!reduce_max_c && g.SP % 4 == 0 && choose_resident(len, batch, true, &L.cfg_idx, &L.P) &&
+        groups * L.P <= 0xF0000000LL && groups <= 0x7fffffffLL) {
+        L.resident = true;
+        L.exch = off;
+        off = align_up(off + resident_ws_bytes(groups, L.P), kWsAlign);
+        L.bytes = off;
+        return L;
+    }
     L.cbuf = off;
     off = align_up(off + (size_t)(g.N * g.Cout * g.SP) * sizeof(float), kWsAlign);
     L.sg = split_geometry(g.N, g.Cout, g.SP, batch, g.SP % 4 == 0);
     L.partials = off;
     off = align_up(off + (size_t)(L.sg.slices * L.sg.chunks) * sizeof(float2), kWsAlign);
     L.stats = off;
-    off = align_up(off + (size_t)(batch ? g.Cout : g.N * g.Cout) * sizeof(GroupStat), kWsAlign);
+    off = align_up(off + (size_t)groups * sizeof(GroupStat), kWsAlign);
     L.bytes = off;
     return L;
 }
@@ -320,40 +374,24 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
     if ((s = check_workspace(workspace, workspace_bytes, L.bytes, fn)) != NR_OK) return s;
 
     int cfg_idx = -1, P = 0;
-    const bool res_ok = vec && choose_resident(S, &cfg_idx, &P) && (P == 1 || L.exchange);
+    const bool res_ok = vec && choose_resident(S, false, false, &cfg_idx, &P) && (P == 1 || L.exchange);
     bool use_res = false;
     if (variant == NR_VARIANT_RESIDENT) {
         if (!res_ok)
             return fail(NR_ERR_UNSUPPORTED,
                         "%s: the resident variant needs 16-byte aligned x/y, S %% 4 == 0 and "
-                        "S <= %lld (S=%lld)", fn,
-                        (long long)kMaxParts * resident_cfg(resident_cfg_count() - 1).part_len,
-                        (long long)S);
+                        "S <= %d (S=%lld)", fn, kMaxParts * 32768, (long long)S);
         use_res = true;
     } else if (variant == NR_VARIANT_AUTO) {
         use_res = res_ok;
     }
 
     if (use_res) {
-        const ResidentCfg cfg = resident_cfg(cfg_idx);
-        ResidentArgs a;
-        a.x = x;
-        a.y = y;
-        a.S = S;
-        a.slices = N * C;
-        a.C = (int32_t)(C > 0x7fffffff ? 0x7fffffff : C);
-        a.P = P;
-        a.eps = eps;
-        a.gamma = gamma;
-        a.beta = beta;
-        a.save_mean = save_mean;
-        a.save_invstd = save_invstd;
-        a.counter = L.exchange ? ws_at<uint32_t>(workspace, L.slots) : nullptr;
-        a.slots = L.exchange ? ws_at<unsigned long long>(workspace, L.slots + kCounterBytes) : nullptr;
-        a.flags = ws_at<uint32_t>(workspace, 0);
-        if (C > 0x7fffffff || a.slices * P > 0xF0000000LL)  // counter headroom for final grabs
+        if (N * C * P > 0xF0000000LL || N * C > 0x7fffffffLL)  // counter headroom, grid limit
             return fail(NR_ERR_UNSUPPORTED, "%s: too many slices for the resident variant", fn);
-        const hipError_t e = launch_resident(cfg, a, stream);
+        const ResidentArgs a = resident_args(x, y, N, C, S, false, P, eps, gamma, beta, 1.0f,
+                                             save_mean, save_invstd, workspace, L.slots, L.exchange);
+        const hipError_t e = launch_resident(resident_cfg(cfg_idx), a, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }
@@ -376,8 +414,8 @@ __attribute__((visibility("default"))) size_t bn_train_workspace_size(int64_t N,
     int64_t total = 0;
     if (N < 1 || check_sizes(N, C, S, &total, "bn_train_workspace_size") != NR_OK) return 0;
     SplitGeom g;
-    size_t p, st;
-    return bn_layout(N, C, S, true, &g, &p, &st);
+    size_t ex, p, st;
+    return bn_layout(N, C, S, true, &g, &ex, &p, &st);
 }
 
 __attribute__((visibility("default"))) nr_status bn_train_forward(
@@ -405,9 +443,18 @@ __attribute__((visibility("default"))) nr_status bn_train_forward(
     if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
     const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
     SplitGeom g;
-    size_t off_p, off_s;
-    const size_t need = bn_layout(N, C, S, vec, &g, &off_p, &off_s);
+    size_t off_x, off_p, off_s;
+    const size_t need = bn_layout(N, C, S, vec, &g, &off_x, &off_p, &off_s);
     if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
+    int cfg_idx = -1, P = 0;
+    if (vec && choose_resident(N * S, true, false, &cfg_idx, &P) && (P == 1 || off_x != 0) &&
+        C * P <= 0xF0000000LL && C <= 0x7fffffffLL) {
+        const ResidentArgs a = resident_args(x, y, N, C, S, true, P, eps, gamma, beta, out_scale,
+                                             save_mean, save_invstd, workspace, off_x, off_x != 0);
+        const hipError_t e = launch_resident(resident_cfg(cfg_idx), a, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     return run_split(g, x, y, eps, gamma, beta, out_scale, save_mean, save_invstd,
                      ws_at<float2>(workspace, off_p), ws_at<GroupStat>(workspace, off_s), stream, fn);
 }
@@ -416,7 +463,7 @@ __attribute__((visibility("default"))) size_t conv_norm_epilogue_workspace_size(
 {
     ConvGeom g;
     if (check_desc(d, &g, "conv_norm_epilogue_workspace_size") != NR_OK) return 0;
-    return chain_layout(g, d->norm == NR_NORM_BATCH_TRAIN).bytes;
+    return chain_layout(g, d->norm == NR_NORM_BATCH_TRAIN, d->reduce_max_c != 0).bytes;
 }
 
 __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
@@ -432,8 +479,25 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (b && !aligned(b, 4)))
         return fail(NR_ERR_MISALIGNED, "%s: tensors must be 4-byte aligned", fn);
     const bool batch = d->norm == NR_NORM_BATCH_TRAIN;
-    const ChainLayout L = chain_layout(g, batch);
+    const ChainLayout L = chain_layout(g, batch, d->reduce_max_c != 0);
     if ((s = check_workspace(workspace, workspace_bytes, L.bytes, fn)) != NR_OK) return s;
+    if (L.resident) {
+        if (!aligned(out, 16))
+            return fail(NR_ERR_MISALIGNED, "%s: out must be 16-byte aligned for this shape", fn);
+        hipError_t e = launch_conv_k3(g, x, w, b, out, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        ResidentArgs a = resident_args(out, out, g.N, g.Cout, g.SP, batch, L.P, d->eps, d->gamma,
+                                       d->beta, d->out_scale, nullptr, nullptr, workspace, L.exch,
+                                       L.P > 1);
+        a.pre_mul = d->pre_mul;
+        a.clamp = d->clamp;
+        a.lo = d->clamp_lo;
+        a.hi = d->clamp_hi;
+        a.post_mul = d->post_mul;
+        e = launch_resident(resident_cfg(L.cfg_idx), a, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     if (L.sg.slices * L.sg.chunks > 0x7fffffffLL)
         return fail(NR_ERR_UNSUPPORTED, "%s: too many statistics chunks for one launch", fn);
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "resident.hpp"
+
 namespace nr {
 
 // ---------------------------------------------------------------------------------------------
@@ -13,53 +15,10 @@ namespace nr {
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kWsAlign = 256;
 constexpr size_t kHeaderBytes = 256;     // uint32 flags at offset 0
-constexpr int kMaxParts = 32;            // parts per slice in the co-resident variant
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// ---------------------------------------------------------------------------------------------
-// Read-once ("resident") instance norm: each slice split over P co-resident workgroups, each
-// holding its part in registers.
-// ---------------------------------------------------------------------------------------------
-struct ResidentCfg {
-    int block;       // threads per workgroup
-    int vec;         // float4 registers per thread (per buffer)
-    int part_len;    // elements per part = block * 4 * vec
-    bool pipelined;  // false: one workgroup per slice (P == 1); true: persistent, P > 1
-};
-
-// The configurations compiled into the library, ascending by part length.
-int resident_cfg_count();
-ResidentCfg resident_cfg(int i);
-
-struct ResidentArgs {
-    const float* x;
-    float* y;
-    int64_t S;        // slice length; S % 4 == 0, x and y 16-B aligned
-    int64_t slices;   // N*C
-    int32_t C;
-    int32_t P;        // parts per slice, 1..kMaxParts
-    float eps;
-    const float* gamma;
-    const float* beta;
-    float* save_mean;
-    float* save_invstd;
-    uint32_t* counter;           // next unit to take; followed (256 B on) by the slots
-    unsigned long long* slots;   // [slices][P][2] tagged exchange words
-    uint32_t* flags;             // sticky error word
-};
-
-// Bytes a launch with P parts uses at `counter` (counter, then slots), zero-filled by
-// launch_resident before every launch.
-constexpr size_t kCounterBytes = 256;
-inline size_t resident_ws_bytes(int64_t slices, int P)
-{
-    return P > 1 ? kCounterBytes + (size_t)slices * (size_t)P * 2 * sizeof(unsigned long long) : 0;
-}
-
-// Largest grid the kernel can have fully co-resident (0 if the configuration is unknown).
-int resident_max_grid(const ResidentCfg& cfg);
-hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStream_t stream);
+// Read-once normalization: see resident.hpp.
 
 // ---------------------------------------------------------------------------------------------
 // Streaming split path: partial statistics per (slice, chunk) -> fixed-order merge per group

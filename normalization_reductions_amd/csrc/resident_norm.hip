@@ -1,0 +1,533 @@
+// resident_norm.hip -- read-once normalization kernels for gfx950: instance norm (statistics
+// per (n, c) slice) and training-mode batch norm (statistics per channel over all n), with an
+// optional fused epilogue.
+//
+// Operations: IN2d page (task l1_p34), statement of the op -- per (n, c) slice, mean and biased
+// variance over the spatial extent, y = (x - mean)/sqrt(var + eps), optionally * gamma[c] +
+// beta[c]. BN page (task l2_p73), opening analysis -- in training mode the same with the batch
+// statistics of each channel over (n, h, w), then x scaling_factor. IN3d page (task l2_p79),
+// its step list -- the multiply before the norm, the clamp and the multiply after it.
+//
+// A "group" is the set of values that share statistics: one slice for instance norm, the N
+// slices of one channel for batch norm. A group of L = members * S values is read in a virtual
+// index space v in [0, L) (member v / S, offset v % S; S % 4 == 0, so a 16-byte vector never
+// straddles two members).
+//
+// Design (MI355X-first; the IN2d page's own kernel reads each slice twice -- a Welford pass
+// and a normalize pass -- which caps a bandwidth-bound kernel at two thirds of the HBM
+// roofline):
+//   * A group is split into P parts (1 <= P <= 32). One workgroup owns a part and keeps it in
+//     VGPRs from load to store, so x crosses HBM exactly once and y once.
+//   * Per thread: 16-byte non-temporal loads; statistics of its own values by the two-pass
+//     formula over registers, relative to a per-group pivot K (the group's first value): the
+//     offset is removed before any sum, the cancellation the IN2d page's numerics discussion
+//     worries about.
+//   * Wave64 butterfly merges of (count, mean, M2) and an LDS combine across waves. Parts
+//     that fill their workgroup give every lane the same count, so those merges use the
+//     equal-count form (no division); ragged parts use the general pairwise update.
+//   * P == 1 (groups up to 64K values): one workgroup per group, hardware dispatch.
+//   * P > 1: a persistent grid of co-resident workgroups (cooperative launch) takes units
+//     (group, part) from an atomic counter in increasing order, so fast CUs take more units
+//     (a static assignment leaves the grid waiting on its slowest CU). Each workgroup holds
+//     two units in two register buffers: it loads the next unit and publishes that unit's
+//     statistics before it waits for the siblings of the unit it loaded before, then
+//     normalizes and stores that one. The wait therefore overlaps a whole unit of memory
+//     traffic instead of stalling it.
+//   * Exchange: (mean, M2) of a part go out as two tagged 64-bit words with relaxed
+//     agent-scope atomic stores; siblings poll them the same way. The counter and slot region
+//     are zero-filled just before every launch, so a non-zero tag marks a word written by
+//     this launch; every exchanged word carries its own validity tag, so no cache-wide
+//     release/acquire fences are needed. The P partials are merged in part order 0..P-1 by
+//     every sibling, so all parts normalize with identical statistics and the result does not
+//     depend on arrival order or on which workgroup took which part.
+//   * Forward progress: a workgroup takes a new unit only after its pending wait finished
+//     and always publishes a unit before its next wait, so every waiting workgroup holds only
+//     published units (at most two). Units are handed out in order, so only the highest group
+//     in flight can miss parts; if every workgroup waited on that group, each would hold two
+//     of its parts, which needs 2G <= P - 1 -- impossible with G >= P co-resident workgroups.
+//   * Normalize from registers with one fused multiply-add per element:
+//     y = d * sc + sh, d = x * pre - K, sc = rstd * gamma * scale,
+//     sh = (beta - mean_d * rstd * gamma) * scale; then the optional clamp and post-multiply.
+#include <stdlib.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "resident.hpp"
+
+namespace nr {
+namespace {
+
+// Tag of an exchange word written by the current launch (the slots start zeroed).
+constexpr uint32_t kTag = 1u;
+
+// Equal-count butterfly: every lane holds the same count; after log2(WIDTH) levels every lane
+// of an aligned group of WIDTH lanes holds the group's statistics.
+template <int WIDTH>
+__device__ __forceinline__ Stat wave_merge_equal(Stat s)
+{
+#pragma unroll
+    for (int off = 1; off < WIDTH; off <<= 1) {
+        const float om = __shfl_xor(s.mean, off);
+        const float oq = __shfl_xor(s.m2, off);
+        const float d = om - s.mean;  // squared below: the sign does not matter
+        s.m2 = (s.m2 + oq) + d * d * (0.5f * s.n);
+        s.mean = (s.mean + om) * 0.5f;
+        s.n *= 2.f;
+    }
+    return s;
+}
+
+// Element offset of virtual index v of group g. Instance groups are one contiguous slice; batch
+// groups walk the N slices of channel g: slice n*C + g. v / S uses a multiply-shift that is
+// exact for v, S < 2^21 (group lengths are capped at 32 parts of 32K values).
+template <bool GROUPED>
+__device__ __forceinline__ int64_t elem_off(const ResidentArgs& a, int64_t g, uint32_t v)
+{
+    if (!GROUPED) return g * a.S + v;
+    const uint32_t m = (uint32_t)(((uint64_t)v * a.div_magic) >> 42);
+    const uint32_t off = v - m * (uint32_t)a.S;
+    return ((int64_t)m * a.C + g) * a.S + off;
+}
+
+// Per-group constants: channel and pre-multiplier (no reads of x: in place, a group's first
+// value may already be overwritten when a part finishes).
+template <bool CHAIN>
+struct GroupConst {
+    int64_t c;
+    float pre;  // pre-multiplier of this channel (1 without the chain epilogue)
+};
+
+template <bool CHAIN>
+__device__ __forceinline__ GroupConst<CHAIN> group_const(const ResidentArgs& a, int64_t g)
+{
+    GroupConst<CHAIN> k;
+    k.c = a.batch ? g : g % a.C;
+    k.pre = (CHAIN && a.pre_mul) ? a.pre_mul[k.c] : 1.f;
+    return k;
+}
+
+// Pivot of group g: its first value, pre-multiplied. Member 0 of either kind of group starts
+// at element g * S. Read when a part is loaded, i.e. before the part publishes -- and no part
+// of the group is written before every part has published.
+template <bool CHAIN>
+__device__ __forceinline__ float group_pivot(const ResidentArgs& a, int64_t g, const GroupConst<CHAIN>& k)
+{
+    return a.x[g * a.S] * k.pre;
+}
+
+// One part held in registers: VEC float4 per thread, already pre-multiplied and pivot-shifted.
+// Instance groups are contiguous: addresses are a workgroup-uniform base plus the lane's
+// offset, and full parts run unpredicated loops. Batch groups compute each vector's address.
+template <int BLOCK, int VEC, bool GROUPED>
+struct Part {
+    f4 v[VEC];
+
+    __device__ __forceinline__ void load(const ResidentArgs& a, int64_t g, uint32_t pstart, int nvec,
+                                         bool full, float pre, float K)
+    {
+        const int tid = threadIdx.x;
+        if (!GROUPED) {
+            const f4* xs = reinterpret_cast<const f4*>(a.x + (g * a.S + pstart));
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) v[j] = ld_stream(xs + j * BLOCK + tid);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) v[j] = v[j] * pre - K;
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int i = j * BLOCK + tid;
+                    v[j] = i < nvec ? ld_stream(xs + i) * pre - K : f4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        } else {
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    v[j] = ld_stream(reinterpret_cast<const f4*>(
+                        a.x + elem_off<true>(a, g, pstart + 4u * (j * BLOCK + tid))));
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) v[j] = v[j] * pre - K;
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int i = j * BLOCK + tid;
+                    v[j] = i < nvec ? ld_stream(reinterpret_cast<const f4*>(
+                                          a.x + elem_off<true>(a, g, pstart + 4u * i))) * pre - K
+                                    : f4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+
+    // This thread's (count, mean, M2): two passes over its registers.
+    __device__ __forceinline__ Stat thread_stat(int nvec, bool full) const
+    {
+        const int tid = threadIdx.x;
+        int nv = VEC;
+        if (!full) {
+            nv = 0;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) nv += (j * BLOCK + tid < nvec) ? 1 : 0;
+        }
+        f4 s = v[0];  // invalid entries are zero, so they add nothing to the sum
+#pragma unroll
+        for (int j = 1; j < VEC; ++j) s += v[j];
+        const float cnt = (float)(4 * nv);
+        const float sum = (s.x + s.y) + (s.z + s.w);
+        const float m = full ? sum * (1.0f / (float)(4 * VEC)) : (nv > 0 ? sum / cnt : 0.f);
+        f4 q = f4{0.f, 0.f, 0.f, 0.f};
+        if (full) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const f4 e = v[j] - m;
+                q += e * e;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                if (j * BLOCK + tid < nvec) {
+                    const f4 e = v[j] - m;
+                    q += e * e;
+                }
+            }
+        }
+        return Stat{cnt, m, (q.x + q.y) + (q.z + q.w)};
+    }
+
+    template <bool CHAIN>
+    __device__ __forceinline__ f4 epilogue(const ResidentArgs& a, f4 d, float sc, float sh, float post) const
+    {
+        f4 z = d * sc + sh;
+        if (CHAIN) {
+            if (a.clamp) {
+                z.x = fminf(fmaxf(z.x, a.lo), a.hi);
+                z.y = fminf(fmaxf(z.y, a.lo), a.hi);
+                z.z = fminf(fmaxf(z.z, a.lo), a.hi);
+                z.w = fminf(fmaxf(z.w, a.lo), a.hi);
+            }
+            z *= post;
+        }
+        return z;
+    }
+
+    template <bool CHAIN>
+    __device__ __forceinline__ void store(const ResidentArgs& a, int64_t g, uint32_t pstart, int nvec,
+                                          bool full, float sc, float sh, float post) const
+    {
+        const int tid = threadIdx.x;
+        if (!GROUPED) {
+            f4* ys = reinterpret_cast<f4*>(a.y + (g * a.S + pstart));
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    st_stream(ys + j * BLOCK + tid, epilogue<CHAIN>(a, v[j], sc, sh, post));
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int i = j * BLOCK + tid;
+                    if (i < nvec) st_stream(ys + i, epilogue<CHAIN>(a, v[j], sc, sh, post));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int i = j * BLOCK + tid;
+                if (full || i < nvec)
+                    st_stream(reinterpret_cast<f4*>(a.y + elem_off<true>(a, g, pstart + 4u * i)),
+                              epilogue<CHAIN>(a, v[j], sc, sh, post));
+            }
+        }
+    }
+};
+
+// Geometry of one unit (group, part).
+struct UnitGeo {
+    int64_t group;
+    uint32_t pstart;  // first virtual index of the part
+    int part, plen, nvec;
+    bool full;
+};
+
+template <int PART>
+__device__ __forceinline__ UnitGeo unit_geo(const ResidentArgs& a, int64_t u)
+{
+    UnitGeo g;
+    g.group = u / a.P;
+    g.part = (int)(u - g.group * a.P);
+    g.pstart = (uint32_t)g.part * PART;
+    const int64_t rem = a.L - (int64_t)g.pstart;
+    g.plen = rem < PART ? (int)rem : PART;
+    g.nvec = g.plen >> 2;
+    g.full = g.plen == PART;
+    return g;
+}
+
+// Statistics of a part: thread stats -> wave merge -> LDS; wave 0 then merges the waves
+// (every lane of wave 0 holds the result). Contains one workgroup barrier.
+template <int BLOCK, int VEC, bool GROUPED>
+__device__ __forceinline__ Stat part_stats(const Part<BLOCK, VEC, GROUPED>& p, const UnitGeo& g,
+                                           Stat* wstat)
+{
+    constexpr int NW = BLOCK / kWave;
+    Stat st = p.thread_stat(g.nvec, g.full);
+    st = g.full ? wave_merge_equal<kWave>(st) : wave_merge<kWave>(st);
+    if (lane_id() == 0) wstat[threadIdx.x / kWave] = st;
+    __syncthreads();
+    Stat w = stat_empty();
+    if (threadIdx.x < kWave) {
+        w = lane_id() < NW ? wstat[lane_id()] : stat_empty();
+        // lanes 0..NW-1 form one aligned group; in a full part all NW counts are equal
+        w = g.full ? wave_merge_equal<NW>(w) : wave_merge<NW>(w);
+    }
+    return w;
+}
+
+// Final per-group coefficients: y = d * fin[0] + fin[1], then * fin[2] (post-multiplier).
+template <bool CHAIN>
+__device__ __forceinline__ void finalize(const ResidentArgs& a, int64_t g, int part,
+                                         const GroupConst<CHAIN>& k, float K, Stat w, float* fin)
+{
+    const float var = w.m2 / w.n;
+    const float rstd = rsqrtf(var + a.eps);
+    const float gm = a.gamma ? a.gamma[k.c] : 1.f;
+    const float bt = a.beta ? a.beta[k.c] : 0.f;
+    const float sc = rstd * gm * a.out_scale;
+    fin[0] = sc;
+    fin[1] = fmaf(-w.mean, sc, bt * a.out_scale);
+    fin[2] = (CHAIN && a.post_mul) ? a.post_mul[k.c] : 1.f;
+    if (part == 0 && a.save_mean) a.save_mean[g] = K + w.mean;
+    if (part == 0 && a.save_invstd) a.save_invstd[g] = rstd;
+}
+
+// ---------------------------------------------------------------------------------------------
+// P == 1: one workgroup per group.
+// ---------------------------------------------------------------------------------------------
+template <int BLOCK, int VEC, bool GROUPED, bool CHAIN>
+__global__ __attribute__((amdgpu_flat_work_group_size(BLOCK, BLOCK), amdgpu_waves_per_eu(4))) void
+norm_single_kernel(ResidentArgs a)
+{
+    constexpr int PART = BLOCK * 4 * VEC;
+    __shared__ Stat wstat[BLOCK / kWave];
+    __shared__ float fin[3];
+    const int64_t grp = blockIdx.x;
+    const UnitGeo g = unit_geo<PART>(a, grp);
+    const GroupConst<CHAIN> k = group_const<CHAIN>(a, grp);
+    const float K = group_pivot<CHAIN>(a, grp, k);
+    Part<BLOCK, VEC, GROUPED> p;
+    p.load(a, grp, 0u, g.nvec, g.full, k.pre, K);
+    const Stat w = part_stats<BLOCK, VEC, GROUPED>(p, g, wstat);
+    if (threadIdx.x == 0) finalize<CHAIN>(a, grp, 0, k, K, w, fin);
+    __syncthreads();
+    p.template store<CHAIN>(a, grp, 0u, g.nvec, g.full, fin[0], fin[1], fin[2]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// P > 1: persistent, two units per workgroup.
+// ---------------------------------------------------------------------------------------------
+// Publish one part's statistics (thread 0).
+__device__ __forceinline__ void publish(const ResidentArgs& a, const UnitGeo& g, Stat w)
+{
+    if (threadIdx.x == 0) {
+        unsigned long long* sl = a.slots + (size_t)g.group * a.P * 2;
+        xchg_store(sl + g.part * 2 + 0, kTag, w.mean);
+        xchg_store(sl + g.part * 2 + 1, kTag, w.m2);
+    }
+}
+
+// Wave 0: wait for all parts of group `grp`, merge them in part order, write fin (lane 0).
+template <int PART, bool CHAIN>
+__device__ __forceinline__ void gather(const ResidentArgs& a, int64_t grp, int part,
+                                       const GroupConst<CHAIN>& k, float K, float* fin)
+{
+    const int lane = lane_id();
+    unsigned long long* sl = a.slots + (size_t)grp * a.P * 2;
+    Stat ps = stat_empty();
+    if (lane < a.P) {
+        unsigned long long w0, w1;
+        uint32_t spins = 0;
+        for (;;) {
+            w0 = xchg_load(sl + lane * 2 + 0);
+            w1 = xchg_load(sl + lane * 2 + 1);
+            if ((uint32_t)(w0 >> 32) == kTag && (uint32_t)(w1 >> 32) == kTag) break;
+            if (++spins > kSpinLimit) {
+                raise_flag(a.flags, kFlagSpinTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const int64_t prem = a.L - (int64_t)lane * PART;
+        ps.n = (float)(prem < PART ? prem : PART);
+        ps.mean = __uint_as_float((uint32_t)w0);
+        ps.m2 = __uint_as_float((uint32_t)w1);
+    }
+    const Stat w = wave_merge<kMaxParts>(ps);  // parts merged in order 0..P-1
+    if (lane == 0) finalize<CHAIN>(a, grp, part, k, K, w, fin);
+}
+
+template <int BLOCK, int VEC, bool GROUPED, bool CHAIN>
+__global__ __attribute__((amdgpu_flat_work_group_size(BLOCK, BLOCK), amdgpu_waves_per_eu(2))) void
+norm_pipelined_kernel(ResidentArgs a)
+{
+    constexpr int PART = BLOCK * 4 * VEC;
+    using PartT = Part<BLOCK, VEC, GROUPED>;
+    __shared__ Stat wstat[BLOCK / kWave];
+    __shared__ float fin[3];
+    __shared__ uint32_t next_unit;
+    const int64_t units = a.groups * a.P;
+
+    // One pipeline step: load unit `un` into `ldp` and publish its statistics (if valid); then
+    // wave 0 waits for the parts of unit `uo` held in `wtp` (if valid) and takes the next unit;
+    // then `wtp` is normalized and stored. Returns the unit taken next.
+    auto step = [&](PartT& ldp, int64_t un, float& Kn, const PartT& wtp, int64_t uo,
+                    float Ko) -> int64_t {
+        if (un < units) {
+            const UnitGeo gn = unit_geo<PART>(a, un);
+            const GroupConst<CHAIN> kn = group_const<CHAIN>(a, gn.group);
+            Kn = group_pivot<CHAIN>(a, gn.group, kn);
+            ldp.load(a, gn.group, gn.pstart, gn.nvec, gn.full, kn.pre, Kn);
+            const Stat w = part_stats<BLOCK, VEC, GROUPED>(ldp, gn, wstat);  // has a barrier
+            publish(a, gn, w);
+        }
+        UnitGeo go{};
+        if (uo < units) go = unit_geo<PART>(a, uo);
+        if (threadIdx.x < kWave) {
+            if (uo < units)
+                gather<PART, CHAIN>(a, go.group, go.part, group_const<CHAIN>(a, go.group), Ko, fin);
+            // after the wait, with every held unit published: take the next unit
+            if (threadIdx.x == 0)
+                next_unit = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const int64_t nx = next_unit;
+        if (uo < units)
+            wtp.template store<CHAIN>(a, go.group, go.pstart, go.nvec, go.full, fin[0], fin[1], fin[2]);
+        __syncthreads();  // fin and next_unit are rewritten by the next step
+        return nx;
+    };
+
+    PartT A, B;
+    float KA = 0.f, KB = 0.f;  // pivots of the units held in A and B
+    if (threadIdx.x == 0)
+        next_unit = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int64_t ua = next_unit;  // unit going into A
+    int64_t ub = units;      // unit held in B (none yet)
+    __syncthreads();
+    for (;;) {
+        const int64_t n1 = step(A, ua, KA, B, ub, KB);  // load A, finish B
+        if (ua >= units) break;                         // A empty, B done
+        ub = n1;
+        const int64_t n2 = step(B, ub, KB, A, ua, KA);  // load B, finish A
+        if (ub >= units) break;                 // B empty, A done
+        ua = n2;
+    }
+}
+
+struct Entry {
+    ResidentCfg cfg;
+    const void* fn;
+};
+
+#define NR_SINGLE(B, V, G, CH)                                                                  \
+    Entry                                                                                       \
+    {                                                                                           \
+        ResidentCfg{B, V, B * 4 * V, false, G, CH},                                             \
+            reinterpret_cast<const void*>(&norm_single_kernel<B, V, G, CH>)                     \
+    }
+#define NR_PIPE(B, V, G, CH)                                                                    \
+    Entry                                                                                       \
+    {                                                                                           \
+        ResidentCfg{B, V, B * 4 * V, true, G, CH},                                              \
+            reinterpret_cast<const void*>(&norm_pipelined_kernel<B, V, G, CH>)                  \
+    }
+
+// For each (grouped, chain) kind: single-workgroup configurations ascending by part length,
+// then the pipelined ones ascending.
+const Entry kCfgs[] = {
+    // instance norm
+    NR_SINGLE(256, 1, false, false), NR_SINGLE(256, 2, false, false), NR_SINGLE(256, 4, false, false),
+    NR_SINGLE(256, 8, false, false), NR_SINGLE(256, 16, false, false), NR_SINGLE(512, 16, false, false),
+    NR_SINGLE(1024, 16, false, false),
+    NR_PIPE(256, 8, false, false), NR_PIPE(256, 16, false, false), NR_PIPE(512, 16, false, false),
+    // batch norm (groups of N slices)
+    NR_SINGLE(256, 4, true, false), NR_SINGLE(256, 16, true, false),
+    NR_PIPE(256, 16, true, false), NR_PIPE(512, 16, true, false),
+    // with the chain epilogue (pre-multiply, clamp, post-multiply)
+    NR_SINGLE(256, 16, false, true), NR_PIPE(256, 16, false, true), NR_PIPE(512, 16, false, true),
+    NR_SINGLE(256, 16, true, true), NR_PIPE(256, 16, true, true), NR_PIPE(512, 16, true, true),
+};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+const void* cfg_fn(const ResidentCfg& c)
+{
+    for (int i = 0; i < kNumCfgs; ++i) {
+        const ResidentCfg& k = kCfgs[i].cfg;
+        if (k.block == c.block && k.vec == c.vec && k.pipelined == c.pipelined &&
+            k.grouped == c.grouped && k.chain == c.chain)
+            return kCfgs[i].fn;
+    }
+    return nullptr;
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* e = getenv(name);
+    if (!e || !*e) return dflt;
+    const int v = atoi(e);
+    return v > 0 ? v : dflt;
+}
+
+}  // namespace
+
+int resident_cfg_count() { return kNumCfgs; }
+ResidentCfg resident_cfg(int i) { return kCfgs[i].cfg; }
+
+uint64_t resident_div_magic(int64_t S) { return ((1ull << 42) + (uint64_t)S - 1) / (uint64_t)S; }
+
+int resident_max_grid(const ResidentCfg& cfg)
+{
+    const void* fn = cfg_fn(cfg);
+    if (!fn) return 0;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, cfg.block, 0) != hipSuccess)
+        return 0;
+    // The pipelined kernel streams best with two workgroups per CU (more of them interleave
+    // more streams into the DRAM pages and lose bandwidth); NORMRED_RESIDENT_WGS_PER_CU
+    // overrides it for tuning.
+    if (cfg.pipelined) {
+        const int want = env_int("NORMRED_RESIDENT_WGS_PER_CU", 2);
+        if (per_cu > want) per_cu = want;
+    }
+    return cus * per_cu;
+}
+
+hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStream_t stream)
+{
+    const void* fn = cfg_fn(cfg);
+    if (!fn) return hipErrorInvalidDeviceFunction;
+    ResidentArgs args = a;
+    void* params[] = {&args};
+    if (!cfg.pipelined) {
+        if (a.P != 1) return hipErrorInvalidValue;
+        const int64_t grid = a.groups;  // validated <= 2^31 - 1 by the caller
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(cfg.block), params, 0, stream);
+    }
+    const int64_t units = a.groups * a.P;
+    int64_t grid = resident_max_grid(cfg);
+    if (grid > units) grid = units;
+    if (grid < a.P) return hipErrorCooperativeLaunchTooLarge;  // the P parts must co-reside
+    // counter + slots start zeroed for every launch (they carry nothing between calls)
+    const hipError_t e = launch_fill_zero(a.counter, resident_ws_bytes(a.groups, a.P), stream);
+    if (e != hipSuccess) return e;
+    const char* coop = getenv("NORMRED_COOPERATIVE");
+    if (coop && coop[0] == '0')  // same grid, regular launch (profilers)
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(cfg.block), params, 0, stream);
+    return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(cfg.block), params, 0, stream);
+}
+
+}  // namespace nr

@@ -302,7 +302,13 @@ def test_inorm_unaligned_and_side_stream(dev, nra, orc):
 # ------------------------------------------------------------------------------------------
 # Training-mode batch norm
 # ------------------------------------------------------------------------------------------
-BN_SHAPES = [(128, 64, 3844), (1, 3, 1), (5, 2, 7), (2, 4, 4100), (3, 1, 100000), (64, 16, 1)]
+BN_SHAPES = [
+    (128, 64, 3844),   # the Conv2d->BN workload's activation: 31 parts per channel (read-once)
+    (1, 3, 1), (5, 2, 7), (64, 16, 1),  # S % 4 != 0: split path
+    (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
+    (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
+    (65, 2, 32768),    # 2.1M values per channel: beyond the read-once index range -> split
+]
 
 
 @pytest.mark.parametrize("shape", BN_SHAPES)
@@ -379,6 +385,9 @@ CHAIN_CASES = [
     ((1, 4, 3, 3), 16, True, False, False),
     ((4, 2, 6, 7, 9), 17, False, True, False),
     ((2, 8, 34, 35), 64, True, False, True),
+    ((1, 2, 260, 260), 3, False, False, True),   # in place, pipelined instance chain (5 parts)
+    ((40, 2, 42, 42), 4, True, False, True),     # in place, pipelined batch chain (4 parts)
+    ((9, 2, 40, 42), 6, True, False, False),     # in place, one workgroup per channel
 ]
 
 
