@@ -14,6 +14,8 @@
 // Chain: IN3d page, its step list and fused elementwise kernel (multiply, normalize, clamp,
 // multiply, max over channels, each output position looping over the channels whose planes
 // are read with coalesced accesses); BN page: normalize with batch statistics, affine, scale.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -86,6 +88,107 @@ __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const f
         conv_point<DIMS, false>(g, x, w, b, c, n, k0, i);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Matrix-core producer: implicit GEMM on v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
+// Rows are output positions, columns output channels, K = (input channel, kd, kh, kw) padded
+// to a multiple of 4 with zeros. Operand layouts of one instruction on gfx950 (checked on the
+// device): A[m][k] comes from lane m + 16k, B[k][n] from lane n + 16k, and D[m][n] lands in lane
+// n + 16*(m/4), register m%4. So lane l = r16 + 16q supplies A for position r16 and tap
+// 4s + q, B for channel r16 and tap 4s + q, and receives channel r16 at 4 consecutive positions
+// 4q..4q+3 -- one 16-byte store per (row tile, channel tile).
+// Each lane keeps its weight fragment (KS x NT values) and its tap offsets into x in VGPRs for
+// the whole wave; A is gathered from x (16 lanes read 16 consecutive positions of one tap).
+// ---------------------------------------------------------------------------------------------
+typedef float mf4 __attribute__((ext_vector_type(4)));
+constexpr int kMfmaBlock = 256;  // 4 waves
+
+template <int DIMS, int KS, int NT, int MT, int TPW>
+__global__ __launch_bounds__(kMfmaBlock) void conv_k3_mfma_kernel(ConvGeom g, const float* __restrict__ x,
+                                                                   const float* __restrict__ w,
+                                                                   const float* __restrict__ b,
+                                                                   float* __restrict__ c)
+{
+    constexpr int KD = DIMS == 3 ? 3 : 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int K = (int)g.Cin * KD * 9;
+    const int plane = (int)(g.H * g.W);
+    const int vol = (int)(g.D * plane);
+
+    int koff[KS];
+    float bw[KS][NT];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int k = 4 * s + q;
+        const bool valid = k < K;
+        const int ci = k / (KD * 9);
+        const int rem = k - ci * (KD * 9);
+        const int kd = rem / 9, kh = (rem % 9) / 3, kw = rem % 3;
+        koff[s] = valid ? ci * vol + kd * plane + kh * (int)g.W + kw : 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bw[s][nt] = valid ? w[(int64_t)(nt * 16 + r16) * K + k] : 0.f;
+    }
+    float bias[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bias[nt] = b ? b[nt * 16 + r16] : 0.f;
+
+    const int64_t n = blockIdx.y;
+    const float* xn = x + n * g.Cin * (int64_t)vol;
+    const int ohw = (int)(g.OH * g.OW);
+    const bool vec_ok = (g.SP & 3) == 0;
+
+    for (int t = 0; t < TPW; ++t) {
+        const int64_t tile0 = (((int64_t)blockIdx.x * TPW + t) * (kMfmaBlock / 64) + wave) * (MT * 16);
+        if (tile0 >= g.SP) break;
+        int pbase[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t m = tile0 + mt * 16 + r16;
+            int od = 0, oh = 0, ow = 0;
+            if (m < g.SP) {
+                const int mm = (int)m;
+                od = DIMS == 3 ? mm / ohw : 0;
+                const int r2 = mm - od * ohw;
+                oh = r2 / (int)g.OW;
+                ow = r2 - oh * (int)g.OW;
+            }
+            pbase[mt] = od * plane + oh * (int)g.W + ow;  // out-of-range rows read position 0
+        }
+        mf4 acc[MT][NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mf4{bias[nt], bias[nt], bias[nt], bias[nt]};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float av[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) av[mt] = xn[pbase[mt] + koff[s]];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bw[s][nt], acc[mt][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t m0 = tile0 + mt * 16 + 4 * q;  // this lane's 4 positions
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float* dst = c + (n * g.Cout + nt * 16 + r16) * g.SP + m0;
+                if (vec_ok && m0 + 3 < g.SP) {
+                    *reinterpret_cast<mf4*>(dst) = acc[mt][nt];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (m0 + r < g.SP) dst[r] = acc[mt][nt][r];
+                }
+            }
+        }
+    }
+}
+
 constexpr int kChainBlock = 256;
 
 __device__ __forceinline__ float chain_value(const ChainArgs& a, int64_t n, int64_t k, float cv)
@@ -98,6 +201,44 @@ __device__ __forceinline__ float chain_value(const ChainArgs& a, int64_t n, int6
     if (a.clamp) z = fminf(fmaxf(z, a.lo), a.hi);
     if (a.post_mul) z *= a.post_mul[k];
     return z;
+}
+
+// Four consecutive positions per thread (SP % 4 == 0, 16-byte aligned planes). The per-(n, k)
+// coefficients are the same for the whole workgroup (n = blockIdx.y), so they come through
+// scalar loads; each channel plane is read with coalesced 16-byte loads.
+__global__ __launch_bounds__(kChainBlock) void chain_apply_vec_kernel(ChainArgs a)
+{
+    const int64_t i4 = (int64_t)blockIdx.x * kChainBlock + threadIdx.x;  // position / 4
+    const int64_t n = blockIdx.y;
+    if (4 * i4 >= a.SP) return;
+    const f4* cp = reinterpret_cast<const f4*>(a.c + n * a.Cout * a.SP) + i4;
+    const int64_t plane4 = a.SP / 4;
+    f4 m = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int64_t k = 0; k < a.Cout; ++k) {
+        const GroupStat s = a.stats[a.batch ? k : n * a.Cout + k];
+        const float pm = a.pre_mul ? a.pre_mul[k] : 1.f;
+        const float A = s.rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale;
+        const float B = (a.beta ? a.beta[k] : 0.f) * a.out_scale;
+        const float qm = a.post_mul ? a.post_mul[k] : 1.f;
+        const f4 cv = ld_stream(cp + k * plane4);
+        f4 z = ((cv * pm - s.pivot) - s.mean_d) * A + B;
+        if (a.clamp) {
+            z.x = fminf(fmaxf(z.x, a.lo), a.hi);
+            z.y = fminf(fmaxf(z.y, a.lo), a.hi);
+            z.z = fminf(fmaxf(z.z, a.lo), a.hi);
+            z.w = fminf(fmaxf(z.w, a.lo), a.hi);
+        }
+        z *= qm;
+        if (a.reduce_max_c) {
+            m.x = fmaxf(m.x, z.x);
+            m.y = fmaxf(m.y, z.y);
+            m.z = fmaxf(m.z, z.z);
+            m.w = fmaxf(m.w, z.w);
+        } else {
+            st_stream(reinterpret_cast<f4*>(a.out + (n * a.Cout + k) * a.SP) + i4, z);
+        }
+    }
+    if (a.reduce_max_c) st_stream(reinterpret_cast<f4*>(a.out + n * a.SP) + i4, m);
 }
 
 __global__ __launch_bounds__(kChainBlock) void chain_apply_kernel(ChainArgs a)
@@ -122,9 +263,36 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_kernel(ChainArgs a)
 
 }  // namespace
 
+namespace {
+template <int DIMS, int KS, int NT, int MT, int TPW>
+hipError_t launch_mfma(const ConvGeom& g, const float* x, const float* w, const float* b, float* c,
+                       hipStream_t stream)
+{
+    const int64_t per_wg = (int64_t)TPW * (kMfmaBlock / 64) * MT * 16;
+    const dim3 grid((unsigned)((g.SP + per_wg - 1) / per_wg), (unsigned)g.N);
+    conv_k3_mfma_kernel<DIMS, KS, NT, MT, TPW><<<grid, dim3(kMfmaBlock), 0, stream>>>(g, x, w, b, c);
+    return hipGetLastError();
+}
+
+bool conv_valu_forced()
+{
+    const char* e = getenv("NORMRED_CONV");
+    return e && e[0] == 'v';  // "valu": the vector-ALU producer (comparisons)
+}
+}  // namespace
+
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream)
 {
+    // Matrix-core producer for the compiled (dims, C_in, C_out) shapes; int32 offsets into one
+    // batch item of x.
+    const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+    if (!conv_valu_forced() && small) {
+        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64)
+            return launch_mfma<2, 18, 4, 4, 4>(g, x, w, b, c, stream);
+        if (g.dims == 3 && g.Cin == 3 && g.Cout == 16)
+            return launch_mfma<3, 21, 1, 8, 4>(g, x, w, b, c, stream);
+    }
     const dim3 grid((unsigned)((g.SP + kConvBlock - 1) / kConvBlock), (unsigned)g.N,
                     (unsigned)((g.Cout + kKB - 1) / kKB));
     if (g.dims == 3)
@@ -136,6 +304,14 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
 
 hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream)
 {
+    const bool vec = (a.SP & 3) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.c) | reinterpret_cast<uintptr_t>(a.out)) & 15) == 0;
+    if (vec) {
+        const int64_t n4 = a.SP / 4;
+        const dim3 grid((unsigned)((n4 + kChainBlock - 1) / kChainBlock), (unsigned)a.N);
+        chain_apply_vec_kernel<<<grid, dim3(kChainBlock), 0, stream>>>(a);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((a.SP + kChainBlock - 1) / kChainBlock), (unsigned)a.N);
     chain_apply_kernel<<<grid, dim3(kChainBlock), 0, stream>>>(a);
     return hipGetLastError();

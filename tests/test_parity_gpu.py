@@ -388,6 +388,11 @@ CHAIN_CASES = [
     ((1, 2, 260, 260), 3, False, False, True),   # in place, pipelined instance chain (5 parts)
     ((40, 2, 42, 42), 4, True, False, True),     # in place, pipelined batch chain (4 parts)
     ((9, 2, 40, 42), 6, True, False, False),     # in place, one workgroup per channel
+    # shapes of the matrix-core producers (2-D C_in 8 -> 64, 3-D C_in 3 -> 16), ragged tails
+    ((2, 8, 15, 13), 64, True, False, True),     # 143 positions: scalar stores, split path
+    ((3, 8, 20, 22), 64, True, False, True),     # 360 positions: 16-byte stores, in place
+    ((2, 3, 6, 9, 11), 16, False, True, True),   # 252 positions, max over channels
+    ((2, 3, 5, 7, 8), 16, False, True, True),    # 90 positions: scalar stores
 ]
 
 
@@ -415,6 +420,22 @@ def test_conv_chain_general(dev, nra, orc, shape, cout, batch, red, full):
     err = maxerr(H(out), ref)
     _log("chain %s Cout %d batch %s max_c %s: max_abs_err %.3e" % (shape, cout, batch, red, err))
     assert err <= TOL
+
+
+def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
+    # the vector-ALU conv producer (used for shapes without a matrix-core instantiation),
+    # forced on the IN3d workload
+    monkeypatch.setenv("NORMRED_CONV", "valu")
+    inp = synth.host_inputs(5)
+    t = lambda a: T(a, dev)
+    out = nra.conv_norm_epilogue_forward(t(inp["x"][:16]), t(inp["w"]), t(inp["b"]),
+                                         norm=nra.NR_NORM_INSTANCE, pre_mul=t(inp["mult"]),
+                                         clamp=inp["clamp"], post_mul=t(inp["mult"]),
+                                         reduce_max_c=True)
+    ref = orc.conv_norm_epilogue(inp["x"][:16], inp["w"], inp["b"], batch=False,
+                                 pre_mul=inp["mult"], clamp=inp["clamp"], post_mul=inp["mult"],
+                                 reduce_max_c=True)
+    assert maxerr(H(out), ref) <= TOL
 
 
 def test_stream_copy(dev, nra):
