@@ -154,7 +154,32 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
     }
 }
 
-template <bool VEC>
+// Normalize pass, 16-byte path: one 1024-value sub-chunk of one slice per workgroup (one
+// vector per thread), a one-shot grid dealt so that each XCD streams a contiguous eighth of
+// the sub-chunks -- the fastest streaming pattern measured on MI355X.
+__global__ __launch_bounds__(kBlock) void split_apply_vec_kernel(SplitGeom g, const float* x, float* y,
+                                                                 const GroupStat* stats,
+                                                                 const float* gamma,
+                                                                 const float* beta, float out_scale,
+                                                                 int64_t subs, int64_t total)
+{
+    int64_t b = blockIdx.x;
+    const int64_t t8 = total / 8 * 8;
+    if (b < t8) b = (b % 8) * (t8 / 8) + b / 8;
+    const int64_t slice = b / subs;
+    const int64_t sub = b - slice * subs;
+    const int64_t c = slice % g.C;
+    const GroupStat s = stats[group_of(g, slice)];
+    const float A = s.rstd * (gamma ? gamma[c] : 1.f) * out_scale;
+    const float B = (beta ? beta[c] : 0.f) * out_scale;
+    const int64_t i = sub * (4 * kBlock) + 4 * threadIdx.x;  // value index in the slice
+    if (i >= g.S) return;
+    const int64_t off = slice * g.S + i;
+    const f4 v = ld_stream(reinterpret_cast<const f4*>(x + off));
+    st_stream(reinterpret_cast<f4*>(y + off), ((v - s.pivot) - s.mean_d) * A + B);
+}
+
+// Normalize pass, scalar path (any alignment or slice length).
 __global__ __launch_bounds__(kBlock) void split_apply_kernel(SplitGeom g, const float* x, float* y,
                                                              const GroupStat* stats,
                                                              const float* gamma,
@@ -171,16 +196,8 @@ __global__ __launch_bounds__(kBlock) void split_apply_kernel(SplitGeom g, const 
     const int64_t start = ch * g.chunk;
     const int64_t len = chunk_len(g, ch);
     const int64_t off = slice * g.S + start;
-    const int tid = threadIdx.x;
-    if (VEC) {
-        const f4* xv = reinterpret_cast<const f4*>(x + off);
-        f4* yv = reinterpret_cast<f4*>(y + off);
-        const int64_t nv = len >> 2;
-        for (int64_t i = tid; i < nv; i += kBlock) st_stream(yv + i, ((ld_stream(xv + i) - K) - md) * A + B);
-    } else {
-        for (int64_t i = tid; i < len; i += kBlock)
-            st_stream1(y + off + i, ((ld_stream1(x + off + i) - K) - md) * A + B);
-    }
+    for (int64_t i = threadIdx.x; i < len; i += kBlock)
+        st_stream1(y + off + i, ((ld_stream1(x + off + i) - K) - md) * A + B);
 }
 
 }  // namespace
@@ -232,11 +249,15 @@ hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
                               const GroupStat* stats, const float* gamma, const float* beta,
                               float out_scale, hipStream_t stream)
 {
-    const int64_t grid = g.slices * g.chunks;
-    if (g.vec)
-        split_apply_kernel<true><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, y, stats, gamma, beta, out_scale);
-    else
-        split_apply_kernel<false><<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, y, stats, gamma, beta, out_scale);
+    const int64_t subs = (g.S + 4 * kBlock - 1) / (4 * kBlock);
+    const int64_t total = g.slices * subs;
+    if (g.vec && total <= 0x7fffffffLL) {
+        split_apply_vec_kernel<<<dim3((unsigned)total), dim3(kBlock), 0, stream>>>(
+            g, x, y, stats, gamma, beta, out_scale, subs, total);
+    } else {
+        const int64_t grid = g.slices * g.chunks;
+        split_apply_kernel<<<dim3((unsigned)grid), dim3(kBlock), 0, stream>>>(g, x, y, stats, gamma, beta, out_scale);
+    }
     return hipGetLastError();
 }
 
