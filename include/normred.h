@@ -118,6 +118,18 @@ nr_status bn_train_forward(const float* x, float* y, int64_t N, int64_t C, int64
                            float* save_mean, float* save_invstd, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* As bn_train_forward, and also blends the batch statistics into running statistics in
+ * place -- BN page, opening analysis: a training step moves running_mean and running_var
+ * toward the batch mean and the UNBIASED batch variance (biased * n / (n - 1), n = N*S) with
+ *     running = (1 - momentum) * running + momentum * batch        (the pages use 0.1).
+ * running_mean, running_var: [C] device buffers, both given or both NULL (no update).
+ * momentum: in [0, 1]. An update needs N*S >= 2 (NR_ERR_INVALID_ARG otherwise). */
+nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, int64_t S,
+                              float eps, const float* gamma, const float* beta, float out_scale,
+                              float* save_mean, float* save_invstd, float momentum,
+                              float* running_mean, float* running_var, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Convolution (k = 3, stride 1, no padding, with bias) -> normalization -> epilogue.
  *
@@ -162,6 +174,9 @@ typedef struct nr_conv_norm_desc {
     float clamp_lo, clamp_hi;    /* used when clamp = 1; lo <= hi */
     const float* post_mul;       /* [C_out] or NULL */
     int32_t reduce_max_c;        /* 0 or 1 */
+    float momentum;              /* running-statistics update (NR_NORM_BATCH_TRAIN only), */
+    float* running_mean;         /* as in bn_train_forward_ex: [C_out] each, both or neither */
+    float* running_var;
 } nr_conv_norm_desc;
 
 /* 0 if the descriptor is invalid. */
@@ -170,6 +185,30 @@ size_t conv_norm_epilogue_workspace_size(const nr_conv_norm_desc* d);
 nr_status conv_norm_epilogue_forward(const nr_conv_norm_desc* d, const float* x, const float* w,
                                      const float* b, float* out, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Convolution (k = 3, stride 1, no padding, with bias) -> eval-mode batch normalization with
+ * running statistics -> x out_scale, folded into one conv pass.
+ *
+ * BN page, its eval-mode discussion: with running statistics the norm is a per-channel affine
+ * map, so it folds into the conv: a_k = gamma[k] * out_scale / sqrt(running_var[k] + eps),
+ * W'[k] = W[k] * a_k, b'[k] = ((b[k] - running_mean[k]) * gamma[k] / sqrt(running_var[k] + eps)
+ * + beta[k]) * out_scale, then out = conv(x, W') + b'.
+ *
+ * d: shapes, eps, gamma, beta, out_scale are used; d->norm must be NR_NORM_BATCH_TRAIN (the
+ *    batch-norm kind; no batch statistics are computed here); pre_mul, post_mul,
+ *    clamp, reduce_max_c and the running-statistics update fields must be unset
+ *    (NR_ERR_UNSUPPORTED otherwise).
+ * running_mean, running_var: [C_out] device buffers (read only).
+ * out: [N, C_out, (D-2,) H-2, W-2]. workspace: >= conv_bn_eval_workspace_size(d) bytes (holds
+ *    the folded weights; refilled by every call).
+ * ------------------------------------------------------------------------------------------ */
+size_t conv_bn_eval_workspace_size(const nr_conv_norm_desc* d);
+
+nr_status conv_bn_eval_forward(const nr_conv_norm_desc* d, const float* x, const float* w,
+                               const float* b, const float* running_mean,
+                               const float* running_var, float* out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Workspace and measurement helpers.

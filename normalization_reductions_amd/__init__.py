@@ -20,7 +20,8 @@ from ._lib import (NR_NORM_BATCH_TRAIN, NR_NORM_INSTANCE, NR_VARIANT_AUTO, NR_VA
                    NR_VARIANT_SPLIT, NormredError, check)
 
 __all__ = [
-    "inorm_forward", "bn_train_forward", "conv_norm_epilogue_forward", "inorm_workspace_size",
+    "inorm_forward", "bn_train_forward", "conv_norm_epilogue_forward", "conv_bn_eval_forward",
+    "inorm_workspace_size",
     "bn_train_workspace_size", "conv_norm_epilogue_workspace_size", "workspace_clear",
     "workspace_check", "stream_copy", "version", "NormredError", "NR_VARIANT_AUTO",
     "NR_VARIANT_RESIDENT", "NR_VARIANT_SPLIT", "NR_NORM_BATCH_TRAIN", "NR_NORM_INSTANCE",
@@ -150,9 +151,10 @@ def bn_train_workspace_size(N: int, C: int, S: int) -> int:
 
 
 def bn_train_forward(x, y=None, *, eps: float = 1e-5, gamma=None, beta=None,
-                     out_scale: float = 1.0, save_mean=None, save_invstd=None, workspace=None,
-                     stream=None):
-    """Training-mode batch norm of x[N, C, *spatial] with batch statistics, then * out_scale."""
+                     out_scale: float = 1.0, save_mean=None, save_invstd=None, running_mean=None,
+                     running_var=None, momentum: float = 0.1, workspace=None, stream=None):
+    """Training-mode batch norm of x[N, C, *spatial] with batch statistics, then * out_scale;
+    running_mean / running_var ([C], both or neither) are updated in place with `momentum`."""
     lib = _lib.load()
     torch = _torch()
     _dev_f32(x, "x")
@@ -166,11 +168,14 @@ def bn_train_forward(x, y=None, *, eps: float = 1e-5, gamma=None, beta=None,
     b = _opt_ptr(beta, "beta", C, x.device)
     sm = _opt_ptr(save_mean, "save_mean", C, x.device)
     si = _opt_ptr(save_invstd, "save_invstd", C, x.device)
+    rm = _opt_ptr(running_mean, "running_mean", C, x.device)
+    rv = _opt_ptr(running_var, "running_var", C, x.device)
     need = bn_train_workspace_size(N, C, S)
     ws = workspace if workspace is not None else get_workspace(need, x.device, stream)
-    check(lib.bn_train_forward(x.data_ptr(), y.data_ptr(), N, C, S, float(eps), g, b,
-                               float(out_scale), sm, si, ctypes.c_void_p(ws.data_ptr()),
-                               ws.numel() * ws.element_size(), _stream(x.device, stream)),
+    check(lib.bn_train_forward_ex(x.data_ptr(), y.data_ptr(), N, C, S, float(eps), g, b,
+                                  float(out_scale), sm, si, float(momentum), rm, rv,
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                  _stream(x.device, stream)),
           "bn_train_forward")
     return y
 
@@ -178,7 +183,8 @@ def bn_train_forward(x, y=None, *, eps: float = 1e-5, gamma=None, beta=None,
 # ---------------------------------------------------------------------------------------------
 # Conv -> normalize -> epilogue
 # ---------------------------------------------------------------------------------------------
-def _desc(x, w, *, norm, eps, pre_mul, gamma, beta, out_scale, clamp, post_mul, reduce_max_c):
+def _desc(x, w, *, norm, eps, pre_mul, gamma, beta, out_scale, clamp, post_mul, reduce_max_c,
+          running_mean=None, running_var=None, momentum=0.1):
     dims = x.dim() - 2
     if dims not in (2, 3):
         raise ValueError("x must be [N, C, H, W] or [N, C, D, H, W]")
@@ -201,6 +207,9 @@ def _desc(x, w, *, norm, eps, pre_mul, gamma, beta, out_scale, clamp, post_mul, 
     d.clamp_lo, d.clamp_hi = (0.0, 0.0) if clamp is None else (float(clamp[0]), float(clamp[1]))
     d.post_mul = _opt_ptr(post_mul, "post_mul", cout, x.device)
     d.reduce_max_c = 1 if reduce_max_c else 0
+    d.momentum = float(momentum)
+    d.running_mean = _opt_ptr(running_mean, "running_mean", cout, x.device)
+    d.running_var = _opt_ptr(running_var, "running_var", cout, x.device)
     osp = tuple(s - 2 for s in sp)
     oshape = (d.N,) + osp if reduce_max_c else (d.N, cout) + osp
     return d, oshape
@@ -212,7 +221,8 @@ def conv_norm_epilogue_workspace_size(desc) -> int:
 
 def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRAIN, eps=1e-5,
                                pre_mul=None, gamma=None, beta=None, out_scale=1.0, clamp=None,
-                               post_mul=None, reduce_max_c=False, workspace=None, stream=None):
+                               post_mul=None, reduce_max_c=False, running_mean=None,
+                               running_var=None, momentum=0.1, workspace=None, stream=None):
     """k=3 valid conv (+bias) -> pre_mul -> batch/instance norm -> gamma, beta -> out_scale ->
     clamp -> post_mul -> optional max over channels (see normred.h)."""
     lib = _lib.load()
@@ -221,7 +231,8 @@ def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRA
     _dev_f32(w, "w")
     d, oshape = _desc(x, w, norm=norm, eps=eps, pre_mul=pre_mul, gamma=gamma, beta=beta,
                       out_scale=out_scale, clamp=clamp, post_mul=post_mul,
-                      reduce_max_c=reduce_max_c)
+                      reduce_max_c=reduce_max_c, running_mean=running_mean,
+                      running_var=running_var, momentum=momentum)
     bp = _opt_ptr(b, "b", d.C_out, x.device)
     if out is None:
         out = torch.empty(oshape, dtype=torch.float32, device=x.device)
@@ -239,6 +250,33 @@ def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRA
                                          ws.numel() * ws.element_size(),
                                          _stream(x.device, stream)),
           "conv_norm_epilogue_forward")
+    return out
+
+
+def conv_bn_eval_forward(x, w, b, running_mean, running_var, out=None, *, eps=1e-5, gamma=None,
+                         beta=None, out_scale=1.0, workspace=None, stream=None):
+    """k=3 valid conv (+bias) -> eval-mode batch norm with running statistics -> * out_scale,
+    folded into the conv weights (see normred.h)."""
+    lib = _lib.load()
+    torch = _torch()
+    _dev_f32(x, "x")
+    _dev_f32(w, "w")
+    d, oshape = _desc(x, w, norm=NR_NORM_BATCH_TRAIN, eps=eps, pre_mul=None, gamma=gamma, beta=beta,
+                      out_scale=out_scale, clamp=None, post_mul=None, reduce_max_c=False)
+    bp = _opt_ptr(b, "b", d.C_out, x.device)
+    rm = _opt_ptr(running_mean, "running_mean", d.C_out, x.device)
+    rv = _opt_ptr(running_var, "running_var", d.C_out, x.device)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=x.device)
+    _dev_f32(out, "out")
+    if tuple(out.shape) != tuple(oshape):
+        raise ValueError("out must have shape %s" % (oshape,))
+    need = int(lib.conv_bn_eval_workspace_size(ctypes.byref(d)))
+    ws = workspace if workspace is not None else get_workspace(max(need, 256), x.device, stream)
+    check(lib.conv_bn_eval_forward(ctypes.byref(d), x.data_ptr(), w.data_ptr(), bp, rm, rv,
+                                   out.data_ptr(), ctypes.c_void_p(ws.data_ptr()),
+                                   ws.numel() * ws.element_size(), _stream(x.device, stream)),
+          "conv_bn_eval_forward")
     return out
 
 

@@ -51,6 +51,9 @@ class ConvNormDesc(ctypes.Structure):
         ("clamp_hi", ctypes.c_float),
         ("post_mul", ctypes.c_void_p),
         ("reduce_max_c", ctypes.c_int32),
+        ("momentum", ctypes.c_float),
+        ("running_mean", ctypes.c_void_p),
+        ("running_var", ctypes.c_void_p),
     ]
 
 
@@ -66,9 +69,14 @@ SIGNATURES = {
     "bn_train_workspace_size": (_sz, [_i64, _i64, _i64]),
     "bn_train_forward": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _f, _vp, _vp, _vp, _sz,
                               _vp]),
+    "bn_train_forward_ex": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _f, _vp, _vp, _f, _vp,
+                                 _vp, _vp, _sz, _vp]),
     "conv_norm_epilogue_workspace_size": (_sz, [ctypes.POINTER(ConvNormDesc)]),
     "conv_norm_epilogue_forward": (_i, [ctypes.POINTER(ConvNormDesc), _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp]),
+    "conv_bn_eval_workspace_size": (_sz, [ctypes.POINTER(ConvNormDesc)]),
+    "conv_bn_eval_forward": (_i, [ctypes.POINTER(ConvNormDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _sz, _vp]),
     "nr_workspace_clear": (_i, [_vp, _sz, _vp]),
     "nr_workspace_check": (_i, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "nr_stream_copy": (_i, [_vp, _vp, _i64, _vp]),

@@ -205,17 +205,35 @@ nr_status check_workspace(void* ws, size_t have, size_t need, const char* fn)
 
 nr_status run_split(const SplitGeom& g, const float* x, float* y, float eps, const float* gamma,
                     const float* beta, float out_scale, float* save_mean, float* save_invstd,
-                    float2* partials, GroupStat* stats, hipStream_t stream, const char* fn)
+                    RunningStats run, float2* partials, GroupStat* stats, hipStream_t stream,
+                    const char* fn)
 {
     if (g.slices * g.chunks > 0x7fffffffLL)
         return fail(NR_ERR_UNSUPPORTED, "%s: %lld slices x %lld chunks exceed one launch", fn,
                     (long long)g.slices, (long long)g.chunks);
     hipError_t e = launch_split_partial(g, x, nullptr, partials, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_merge(g, x, nullptr, partials, eps, stats, save_mean, save_invstd, stream);
+    e = launch_split_merge(g, x, nullptr, partials, eps, stats, save_mean, save_invstd, run, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_split_apply(g, x, y, stats, gamma, beta, out_scale, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
+    return NR_OK;
+}
+
+// Validate an optional running-statistics update: both buffers or neither, 4-byte aligned,
+// momentum in [0, 1], at least two values per channel (the unbiased variance divides by n - 1).
+nr_status check_running(const float* rm, const float* rv, float momentum, int64_t count,
+                        const char* fn)
+{
+    if ((rm == nullptr) != (rv == nullptr))
+        return fail(NR_ERR_INVALID_ARG, "%s: running_mean and running_var must both be given or both be NULL", fn);
+    if (!rm) return NR_OK;
+    if (!aligned(rm, 4) || !aligned(rv, 4))
+        return fail(NR_ERR_MISALIGNED, "%s: running statistics must be 4-byte aligned", fn);
+    if (!std::isfinite(momentum) || momentum < 0.f || momentum > 1.f)
+        return fail(NR_ERR_INVALID_ARG, "%s: momentum must be in [0, 1]", fn);
+    if (count < 2)
+        return fail(NR_ERR_INVALID_ARG, "%s: running variance needs >= 2 values per channel", fn);
     return NR_OK;
 }
 
@@ -264,6 +282,15 @@ nr_status check_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
     if ((s = check_opt(d->gamma, "gamma", fn)) != NR_OK) return s;
     if ((s = check_opt(d->beta, "beta", fn)) != NR_OK) return s;
     if ((s = check_opt(d->post_mul, "post_mul", fn)) != NR_OK) return s;
+    if (d->running_mean || d->running_var) {
+        if (d->norm != NR_NORM_BATCH_TRAIN)
+            return fail(NR_ERR_INVALID_ARG, "%s: running statistics need NR_NORM_BATCH_TRAIN", fn);
+        const int64_t per_channel = d->N * (d->spatial_dims == 3 ? d->in_d - 2 : 1) *
+                                    (d->in_h - 2) * (d->in_w - 2);
+        if ((s = check_running(d->running_mean, d->running_var, d->momentum,
+                               d->N == 0 ? 2 : per_channel, fn)) != NR_OK)
+            return s;
+    }
     ConvGeom c;
     c.dims = d->spatial_dims;
     c.N = d->N;
@@ -396,7 +423,7 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }
-    return run_split(L.sg, x, y, eps, gamma, beta, 1.0f, save_mean, save_invstd,
+    return run_split(L.sg, x, y, eps, gamma, beta, 1.0f, save_mean, save_invstd, RunningStats{},
                      ws_at<float2>(workspace, L.partials), ws_at<GroupStat>(workspace, L.stats),
                      stream, fn);
 }
@@ -419,10 +446,11 @@ __attribute__((visibility("default"))) size_t bn_train_workspace_size(int64_t N,
     return bn_layout(N, C, S, true, &g, &ex, &p, &st);
 }
 
-__attribute__((visibility("default"))) nr_status bn_train_forward(
+__attribute__((visibility("default"))) nr_status bn_train_forward_ex(
     const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps, const float* gamma,
-    const float* beta, float out_scale, float* save_mean, float* save_invstd, void* workspace,
-    size_t workspace_bytes, hipStream_t stream)
+    const float* beta, float out_scale, float* save_mean, float* save_invstd, float momentum,
+    float* running_mean, float* running_var, void* workspace, size_t workspace_bytes,
+    hipStream_t stream)
 {
     static const char* fn = "bn_train_forward";
     if (N < 1) return fail(NR_ERR_INVALID_ARG, "%s: batch statistics need N >= 1", fn);
@@ -442,6 +470,8 @@ __attribute__((visibility("default"))) nr_status bn_train_forward(
     if ((s = check_opt(beta, "beta", fn)) != NR_OK) return s;
     if ((s = check_opt(save_mean, "save_mean", fn)) != NR_OK) return s;
     if ((s = check_opt(save_invstd, "save_invstd", fn)) != NR_OK) return s;
+    if ((s = check_running(running_mean, running_var, momentum, N * S, fn)) != NR_OK) return s;
+    const RunningStats run{running_mean, running_var, momentum};
     const bool vec = aligned(x, 16) && aligned(y, 16) && S % 4 == 0;
     SplitGeom g;
     size_t off_x, off_p, off_s;
@@ -450,14 +480,26 @@ __attribute__((visibility("default"))) nr_status bn_train_forward(
     int cfg_idx = -1, P = 0;
     if (vec && choose_resident(N * S, true, false, &cfg_idx, &P) && (P == 1 || off_x != 0) &&
         C * P <= 0xF0000000LL && C <= 0x7fffffffLL) {
-        const ResidentArgs a = resident_args(x, y, N, C, S, true, P, eps, gamma, beta, out_scale,
-                                             save_mean, save_invstd, workspace, off_x, off_x != 0);
+        ResidentArgs a = resident_args(x, y, N, C, S, true, P, eps, gamma, beta, out_scale,
+                                       save_mean, save_invstd, workspace, off_x, off_x != 0);
+        a.running_mean = running_mean;
+        a.running_var = running_var;
+        a.momentum = momentum;
         const hipError_t e = launch_resident(resident_cfg(cfg_idx), a, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }
-    return run_split(g, x, y, eps, gamma, beta, out_scale, save_mean, save_invstd,
+    return run_split(g, x, y, eps, gamma, beta, out_scale, save_mean, save_invstd, run,
                      ws_at<float2>(workspace, off_p), ws_at<GroupStat>(workspace, off_s), stream, fn);
+}
+
+__attribute__((visibility("default"))) nr_status bn_train_forward(
+    const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps, const float* gamma,
+    const float* beta, float out_scale, float* save_mean, float* save_invstd, void* workspace,
+    size_t workspace_bytes, hipStream_t stream)
+{
+    return bn_train_forward_ex(x, y, N, C, S, eps, gamma, beta, out_scale, save_mean, save_invstd,
+                               0.f, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 __attribute__((visibility("default"))) size_t conv_norm_epilogue_workspace_size(const nr_conv_norm_desc* d)
@@ -495,6 +537,9 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         a.lo = d->clamp_lo;
         a.hi = d->clamp_hi;
         a.post_mul = d->post_mul;
+        a.running_mean = d->running_mean;
+        a.running_var = d->running_var;
+        a.momentum = d->momentum;
         e = launch_resident(resident_cfg(L.cfg_idx), a, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
@@ -509,7 +554,8 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_split_partial(L.sg, c, d->pre_mul, partials, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_merge(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr, stream);
+    e = launch_split_merge(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr,
+                           RunningStats{d->running_mean, d->running_var, d->momentum}, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     ChainArgs a;
     a.c = c;
@@ -529,6 +575,65 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     a.post_mul = d->post_mul;
     a.reduce_max_c = d->reduce_max_c;
     e = launch_chain_apply(a, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return NR_OK;
+}
+
+// Eval-mode conv + batch norm: workspace = folded weights then folded bias.
+size_t bn_eval_layout(const ConvGeom& g, size_t* off_b)
+{
+    const int64_t K = g.Cin * (g.dims == 3 ? 27 : 9);
+    size_t off = kHeaderBytes;
+    off = align_up(off + (size_t)(g.Cout * K) * sizeof(float), kWsAlign);
+    *off_b = off;
+    return align_up(off + (size_t)g.Cout * sizeof(float), kWsAlign);
+}
+
+nr_status check_eval_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
+{
+    nr_status s = check_desc(d, g, fn);
+    if (s != NR_OK) return s;
+    if (d->norm != NR_NORM_BATCH_TRAIN)
+        return fail(NR_ERR_INVALID_ARG, "%s: norm must be NR_NORM_BATCH_TRAIN", fn);
+    if (d->pre_mul || d->post_mul || d->clamp || d->reduce_max_c || d->running_mean || d->running_var)
+        return fail(NR_ERR_UNSUPPORTED,
+                    "%s: eval mode supports gamma, beta and out_scale only (no pre/post multiply, "
+                    "clamp, max over channels or running-statistics update)", fn);
+    return NR_OK;
+}
+
+__attribute__((visibility("default"))) size_t conv_bn_eval_workspace_size(const nr_conv_norm_desc* d)
+{
+    ConvGeom g;
+    if (check_eval_desc(d, &g, "conv_bn_eval_workspace_size") != NR_OK) return 0;
+    size_t ob;
+    return bn_eval_layout(g, &ob);
+}
+
+__attribute__((visibility("default"))) nr_status conv_bn_eval_forward(
+    const nr_conv_norm_desc* d, const float* x, const float* w, const float* b,
+    const float* running_mean, const float* running_var, float* out, void* workspace,
+    size_t workspace_bytes, hipStream_t stream)
+{
+    static const char* fn = "conv_bn_eval_forward";
+    ConvGeom g;
+    nr_status s = check_eval_desc(d, &g, fn);
+    if (s != NR_OK) return s;
+    if (g.N == 0) return NR_OK;  // empty batch
+    if (!x || !w || !out || !running_mean || !running_var)
+        return fail(NR_ERR_INVALID_ARG, "%s: x, w, running_mean, running_var and out must be non-NULL", fn);
+    if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (b && !aligned(b, 4)) ||
+        !aligned(running_mean, 4) || !aligned(running_var, 4))
+        return fail(NR_ERR_MISALIGNED, "%s: tensors must be 4-byte aligned", fn);
+    size_t off_b;
+    const size_t need = bn_eval_layout(g, &off_b);
+    if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
+    float* wf = ws_at<float>(workspace, kHeaderBytes);
+    float* bf = ws_at<float>(workspace, off_b);
+    hipError_t e = launch_fold_bn_eval(g, w, b, running_mean, running_var, d->gamma, d->beta,
+                                       d->eps, d->out_scale, wf, bf, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_conv_k3(g, x, wf, bf, out, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return NR_OK;
 }

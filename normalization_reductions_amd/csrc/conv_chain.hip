@@ -189,6 +189,30 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_mfma_kernel(ConvGeom g, co
     }
 }
 
+// Eval-mode batch norm folded into the conv (BN page, its eval-mode discussion): per output
+// channel k, a = gamma * scale / sqrt(rv + eps); W'[k][.] = W[k][.] * a and
+// b' = ((b - rm) * gamma / sqrt(rv + eps) + beta) * scale. One workgroup per channel.
+__global__ __launch_bounds__(256) void fold_bn_eval_kernel(const float* __restrict__ w,
+                                                           const float* __restrict__ b,
+                                                           const float* __restrict__ rm,
+                                                           const float* __restrict__ rv,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ beta,
+                                                           float eps, float scale, int64_t K,
+                                                           float* __restrict__ wf, float* __restrict__ bf)
+{
+    const int64_t k = blockIdx.x;
+    const float inv = 1.0f / sqrtf(rv[k] + eps);
+    const float g = gamma ? gamma[k] : 1.f;
+    const float a = g * inv * scale;
+    for (int64_t j = threadIdx.x; j < K; j += 256) wf[k * K + j] = w[k * K + j] * a;
+    if (threadIdx.x == 0) {
+        const float bb = b ? b[k] : 0.f;
+        const float bt = beta ? beta[k] : 0.f;
+        bf[k] = ((bb - rm[k]) * g * inv + bt) * scale;
+    }
+}
+
 constexpr int kChainBlock = 256;
 
 __device__ __forceinline__ float chain_value(const ChainArgs& a, int64_t n, int64_t k, float cv)
@@ -317,4 +341,16 @@ hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+}  // namespace nr
+
+namespace nr {
+hipError_t launch_fold_bn_eval(const ConvGeom& g, const float* w, const float* b, const float* rm,
+                               const float* rv, const float* gamma, const float* beta, float eps,
+                               float scale, float* wf, float* bf, hipStream_t stream)
+{
+    const int64_t K = g.Cin * (g.dims == 3 ? 27 : 9);
+    fold_bn_eval_kernel<<<dim3((unsigned)g.Cout), dim3(256), 0, stream>>>(w, b, rm, rv, gamma, beta,
+                                                                         eps, scale, K, wf, bf);
+    return hipGetLastError();
+}
 }  // namespace nr

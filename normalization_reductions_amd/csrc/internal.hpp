@@ -45,9 +45,16 @@ SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec);
 
 hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
                                 float2* partials, hipStream_t stream);
+struct RunningStats {      // optional in-place running-statistics update (batch groups)
+    float* mean = nullptr;
+    float* var = nullptr;
+    float momentum = 0.f;
+};
+
 hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
                               const float2* partials, float eps, GroupStat* stats,
-                              float* save_mean, float* save_invstd, hipStream_t stream);
+                              float* save_mean, float* save_invstd, RunningStats run,
+                              hipStream_t stream);
 hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
                               const GroupStat* stats, const float* gamma, const float* beta,
                               float out_scale, hipStream_t stream);
@@ -64,6 +71,11 @@ struct ConvGeom {
 
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream);
+
+// Eval-mode batch norm folded into conv weights: wf [Cout][Cin*k^dims], bf [Cout].
+hipError_t launch_fold_bn_eval(const ConvGeom& g, const float* w, const float* b, const float* rm,
+                               const float* rv, const float* gamma, const float* beta, float eps,
+                               float scale, float* wf, float* bf, hipStream_t stream);
 
 struct ChainArgs {
     const float* c;        // [N, Cout, SP] conv output

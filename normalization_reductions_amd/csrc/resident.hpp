@@ -46,6 +46,9 @@ struct ResidentArgs {
     const float* post_mul;  // chain kernels: [C] or NULL
     float* save_mean;       // [groups] or NULL
     float* save_invstd;     // [groups] or NULL
+    float* running_mean;    // [groups] or NULL: updated in place (batch groups)
+    float* running_var;     // [groups] or NULL (unbiased batch variance blended in)
+    float momentum;
     uint32_t* counter;           // next unit to take; followed (256 B on) by the slots
     unsigned long long* slots;   // [groups][P][2] tagged exchange words
     uint32_t* flags;             // sticky error word

@@ -45,6 +45,8 @@
 //     published units (at most two). Units are handed out in order, so only the highest group
 //     in flight can miss parts; if every workgroup waited on that group, each would hold two
 //     of its parts, which needs 2G <= P - 1 -- impossible with G >= P co-resident workgroups.
+//   * Batch groups can also blend their statistics into running mean/variance buffers (the
+//     group's part 0 does it once per launch).
 //   * Normalize from registers with one fused multiply-add per element:
 //     y = d * sc + sh, d = x * pre - K, sc = rstd * gamma * scale,
 //     sh = (beta - mean_d * rstd * gamma) * scale; then the optional clamp and post-multiply.
@@ -298,6 +300,13 @@ __device__ __forceinline__ void finalize(const ResidentArgs& a, int64_t g, int p
     fin[2] = (CHAIN && a.post_mul) ? a.post_mul[k.c] : 1.f;
     if (part == 0 && a.save_mean) a.save_mean[g] = K + w.mean;
     if (part == 0 && a.save_invstd) a.save_invstd[g] = rstd;
+    if (part == 0 && a.running_mean) {
+        // BN page, opening analysis: running = (1 - m) * running + m * batch, the variance
+        // unbiased (times n / (n - 1))
+        const float m = a.momentum;
+        a.running_mean[g] = (1.f - m) * a.running_mean[g] + m * (K + w.mean);
+        a.running_var[g] = (1.f - m) * a.running_var[g] + m * (w.m2 / (w.n - 1.f));
+    }
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
                                                             const float* pre_mul,
                                                             const float2* partials, float eps,
                                                             GroupStat* stats, float* save_mean,
-                                                            float* save_invstd)
+                                                            float* save_invstd, RunningStats run)
 {
     const int64_t grp = blockIdx.x;
     const int lane = threadIdx.x;
@@ -151,6 +151,13 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
         stats[grp] = GroupStat{K, st.mean, rstd, 0.f};
         if (save_mean) save_mean[grp] = K + st.mean;
         if (save_invstd) save_invstd[grp] = rstd;
+        if (run.mean) {
+            // BN page, opening analysis: running = (1 - m) * running + m * batch, with the
+            // unbiased batch variance
+            const float m = run.momentum;
+            run.mean[grp] = (1.f - m) * run.mean[grp] + m * (K + st.mean);
+            run.var[grp] = (1.f - m) * run.var[grp] + m * (st.m2 / (st.n - 1.f));
+        }
     }
 }
 
@@ -237,11 +244,12 @@ hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float*
 
 hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
                               const float2* partials, float eps, GroupStat* stats,
-                              float* save_mean, float* save_invstd, hipStream_t stream)
+                              float* save_mean, float* save_invstd, RunningStats run,
+                              hipStream_t stream)
 {
     const int64_t groups = g.batch ? g.C : g.slices;
     split_merge_kernel<<<dim3((unsigned)groups), dim3(kWave), 0, stream>>>(
-        g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
+        g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, run);
     return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ def _load():
     lib.or_conv_k3.restype = ci
     lib.or_batch_norm_train.argtypes = [vp, vp, i64, i64, i64, dbl, vp, vp, dbl, vp, vp, ci]
     lib.or_batch_norm_train.restype = ci
+    lib.or_conv_bn_eval.argtypes = [vp, vp, vp, vp, vp, vp, vp, dbl, dbl, vp, ci, i64, i64, i64,
+                                    i64, i64, i64, ci]
+    lib.or_conv_bn_eval.restype = ci
+    lib.or_bn_running_update.argtypes = [vp, vp, i64, i64, dbl, vp, vp]
+    lib.or_bn_running_update.restype = ci
     lib.or_conv_norm_epilogue.argtypes = [
         vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
         ci, dbl, vp, vp, vp, dbl, ci, dbl, dbl, vp, ci, vp, vp, ci]
@@ -149,6 +154,22 @@ def batch_norm_train(x, eps=1e-5, gamma=None, beta=None, scale=1.0, nthreads=0, 
     return (y, mean, var) if with_stats else y
 
 
+def bn_running_update(mean, var, count, running_mean, running_var, momentum=0.1):
+    """Running-statistics step of training-mode batch norm (BN page, opening analysis):
+    running = (1 - momentum) * running + momentum * batch, with the unbiased batch variance
+    var * count / (count - 1). mean/var are the fp64 batch statistics (var biased). Returns the
+    updated fp32 running mean and variance (new arrays)."""
+    mean = np.ascontiguousarray(mean, dtype=np.float64)
+    var = np.ascontiguousarray(var, dtype=np.float64)
+    rm = np.array(running_mean, dtype=np.float32, copy=True)
+    rv = np.array(running_var, dtype=np.float32, copy=True)
+    rc = _load().or_bn_running_update(_ptr(mean), _ptr(var), mean.size, int(count), float(momentum),
+                                      _ptr(rm), _ptr(rv))
+    if rc != 0:
+        raise ValueError("or_bn_running_update rejected its arguments")
+    return rm, rv
+
+
 def conv_norm_epilogue(x, w, b, *, batch, eps=1e-5, pre_mul=None, gamma=None, beta=None,
                        out_scale=1.0, clamp=None, post_mul=None, reduce_max_c=False, nthreads=0,
                        with_stats=False):
@@ -182,3 +203,27 @@ def conv_norm_epilogue(x, w, b, *, batch, eps=1e-5, pre_mul=None, gamma=None, be
     if rc != 0:
         raise ValueError("or_conv_norm_epilogue rejected its arguments")
     return (out, mean, inv) if with_stats else out
+
+
+def conv_bn_eval(x, w, b, running_mean, running_var, *, gamma=None, beta=None, eps=1e-5,
+                 scale=1.0, nthreads=0):
+    """Conv k=3 then eval-mode batch norm with running statistics, then * scale (BN page, its
+    eval-mode discussion), unfolded: ((conv(x) - rm)/sqrt(rv + eps) * gamma + beta) * scale."""
+    x, w, b = _f32(x), _f32(w), _f32(b)
+    rm, rv, g, bt = _f32(running_mean), _f32(running_var), _f32(gamma), _f32(beta)
+    dims = x.ndim - 2
+    N, Cin = x.shape[0], x.shape[1]
+    Cout = w.shape[0]
+    if dims == 2:
+        D, (H, W) = 1, x.shape[2:]
+        oshape = (N, Cout, H - 2, W - 2)
+    else:
+        D, H, W = x.shape[2:]
+        oshape = (N, Cout, D - 2, H - 2, W - 2)
+    out = np.empty(oshape, np.float32)
+    rc = _load().or_conv_bn_eval(_ptr(x), _ptr(w), _ptr(b), _ptr(rm), _ptr(rv), _ptr(g), _ptr(bt),
+                                 float(eps), float(scale), _ptr(out), dims, N, Cin, Cout, D, H, W,
+                                 int(nthreads))
+    if rc != 0:
+        raise ValueError("or_conv_bn_eval rejected its arguments")
+    return out

@@ -271,6 +271,26 @@ OR_API int or_batch_norm_train(const double* x, float* y, int64_t N, int64_t C, 
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Running statistics of training-mode batch norm.                                            */
+/*                                                                                            */
+/* BN page, opening analysis: a training-mode step also moves the running mean and variance  */
+/* toward the batch statistics with momentum 0.1 -- running = (1 - m) * running + m * batch   */
+/* -- and the running variance takes the unbiased batch variance (biased * n / (n - 1)).      */
+/* mean/var: [C] batch statistics (var biased); count: values per channel (>= 2).            */
+/* ------------------------------------------------------------------------------------------ */
+OR_API int or_bn_running_update(const double* mean, const double* var, int64_t C, int64_t count,
+                                double momentum, float* running_mean, float* running_var)
+{
+    if (!mean || !var || !running_mean || !running_var || C < 0 || count < 2) return -1;
+    for (int64_t c = 0; c < C; ++c) {
+        const double unbiased = var[c] * (double)count / (double)(count - 1);
+        running_mean[c] = (float)((1.0 - momentum) * (double)running_mean[c] + momentum * mean[c]);
+        running_var[c] = (float)((1.0 - momentum) * (double)running_var[c] + momentum * unbiased);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* The general conv -> normalize -> epilogue chain.                                           */
 /*                                                                                            */
 /* Step order (both pages' models are instances of it):                                       */
@@ -429,4 +449,39 @@ done:
     free(mean);
     free(inv);
     return rc;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Conv followed by eval-mode batch norm (running statistics), then a scale.                 */
+/*                                                                                            */
+/* BN page, its eval-mode discussion: in eval mode the norm uses the running statistics,     */
+/* y = ((conv(x) - running_mean) / sqrt(running_var + eps) * gamma + beta) * scale. The page */
+/* folds this into the conv weights; the oracle keeps the unfolded definition (fp64 conv,    */
+/* then the per-channel affine map, one final rounding).                                     */
+/* ------------------------------------------------------------------------------------------ */
+OR_API int or_conv_bn_eval(const float* x, const float* w, const float* b, const float* running_mean,
+                           const float* running_var, const float* gamma, const float* beta,
+                           double eps, double scale, float* out, int dims, int64_t N, int64_t Cin,
+                           int64_t Cout, int64_t D, int64_t H, int64_t W, int nthreads)
+{
+    if (!out || !running_mean || !running_var || N <= 0) return -1;
+    const int64_t SP = (dims == 3 ? (D - 2) : 1) * (H - 2) * (W - 2);
+    double* c = (double*)malloc(sizeof(double) * (size_t)(N * Cout * SP));
+    if (!c) return -1;
+    if (or_conv_k3(x, w, b, c, dims, N, Cin, Cout, D, H, W, nthreads) != 0) {
+        free(c);
+        return -1;
+    }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < Cout; ++k) {
+            const double inv = 1.0 / sqrt((double)running_var[k] + eps);
+            const double g = gamma ? (double)gamma[k] : 1.0;
+            const double bt = beta ? (double)beta[k] : 0.0;
+            const double* cp = c + (n * Cout + k) * SP;
+            float* op = out + (n * Cout + k) * SP;
+            for (int64_t i = 0; i < SP; ++i)
+                op[i] = (float)((((cp[i] - (double)running_mean[k]) * inv) * g + bt) * scale);
+        }
+    free(c);
+    return 0;
 }

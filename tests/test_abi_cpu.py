@@ -44,15 +44,27 @@ def test_version(lib):
     assert b"gfx950" in lib.nr_version()
 
 
-def test_desc_struct_layout_matches_header():
-    # offsets the C compiler gives nr_conv_norm_desc (x86-64 SysV): ints 4, int64/pointers 8
+def test_desc_struct_layout_matches_header(tmp_path):
+    # the ctypes mirror must give every field of nr_conv_norm_desc the offset the C compiler does
+    import shutil
+    import subprocess
+
     from normalization_reductions_amd._lib import ConvNormDesc as D
 
-    assert D.spatial_dims.offset == 0 and D.ksize.offset == 4 and D.N.offset == 8
-    assert D.in_w.offset == 48 and D.norm.offset == 56 and D.eps.offset == 60
-    assert D.pre_mul.offset == 64 and D.beta.offset == 80 and D.out_scale.offset == 88
-    assert D.clamp.offset == 92 and D.clamp_hi.offset == 100 and D.post_mul.offset == 104
-    assert D.reduce_max_c.offset == 112 and ctypes.sizeof(D) == 120
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("needs gcc and the ROCm headers")
+    names = [f[0] for f in D._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"normred.h\"\nint main(void) {\n"
+                   + "".join('printf("%%zu\\n", offsetof(nr_conv_norm_desc, %s));\n' % n for n in names)
+                   + 'printf("%zu\\n", sizeof(nr_conv_norm_desc));\nreturn 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[:-1] == [getattr(D, n).offset for n in names]
+    assert got[-1] == ctypes.sizeof(D)
 
 
 def test_workspace_sizes(lib):
@@ -116,6 +128,21 @@ def test_bn_rejects(lib):
     assert f(FAKE + 1, FAKE + 1, 1, 1, 4, 1e-5, None, None, 1.0, None, None, FAKE, 1 << 20, None) == 2
 
 
+def _bn_ex(lib, momentum=0.1, rm=FAKE + (1 << 38), rv=FAKE + (1 << 39), N=2, S=4):
+    return lib.bn_train_forward_ex(FAKE, FAKE + (1 << 36), N, 3, S, 1e-5, None, None, 1.0, None,
+                                   None, momentum, rm, rv, FAKE + (1 << 37), 1 << 20, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(momentum=-0.1), 1), (dict(momentum=1.5), 1), (dict(momentum=float("nan")), 1),
+    (dict(rm=None), 1), (dict(rv=None), 1), (dict(rm=FAKE + (1 << 38) + 2), 2),
+    (dict(N=1, S=1), 1),  # one value per channel: no unbiased variance
+])
+def test_bn_running_stats_rejects(lib, kw, status):
+    assert _bn_ex(lib, **kw) == status
+    assert "bn_train_forward" in lib.nr_last_error().decode()
+
+
 def _desc(**over):
     from normalization_reductions_amd._lib import ConvNormDesc
 
@@ -140,6 +167,44 @@ def test_conv_rejects(lib, over, status):
     r = lib.conv_norm_epilogue_forward(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
     assert r == status
     assert lib.conv_norm_epilogue_workspace_size(ctypes.byref(d)) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(norm=2, running_mean=FAKE, running_var=FAKE + 64), 1),  # instance norm keeps none
+    (dict(running_mean=FAKE), 1), (dict(running_mean=FAKE, running_var=FAKE + 64, momentum=2.0), 1),
+    (dict(running_mean=FAKE + 1, running_var=FAKE + 64), 2),
+    (dict(N=1, in_h=3, in_w=3, running_mean=FAKE, running_var=FAKE + 64), 1),  # 1 value/channel
+])
+def test_conv_running_stats_rejects(lib, over, status):
+    d = _desc(**over)
+    r = lib.conv_norm_epilogue_forward(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert r == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(norm=2), 1), (dict(pre_mul=FAKE), 3), (dict(post_mul=FAKE), 3), (dict(clamp=1), 3),
+    (dict(reduce_max_c=1), 3), (dict(running_mean=FAKE, running_var=FAKE + 64), 3),
+    (dict(ksize=5), 3), (dict(eps=float("nan")), 1),
+])
+def test_conv_bn_eval_rejects(lib, over, status):
+    d = _desc(**over)
+    f = lib.conv_bn_eval_forward
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == status
+    assert lib.conv_bn_eval_workspace_size(ctypes.byref(d)) == 0
+    assert lib.nr_last_error().decode().startswith("conv_bn_eval")
+
+
+def test_conv_bn_eval_rejects_pointers_and_workspace(lib):
+    d = _desc()
+    need = lib.conv_bn_eval_workspace_size(ctypes.byref(d))
+    assert need >= 256 + 4 * (4 * 3 * 9 + 4)
+    f = lib.conv_bn_eval_forward
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, need, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, FAKE, FAKE, need, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 4
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE, need, None) == 2
+    d0 = _desc(N=0)
+    assert f(ctypes.byref(d0), None, None, None, None, None, None, None, 0, None) == 0
 
 
 def test_conv_rejects_pointers_and_workspace(lib):

@@ -258,6 +258,30 @@ def test_bn_matches_torch_float64(oracle_mod):
     np.testing.assert_allclose(y, ref, rtol=0, atol=1e-6)
 
 
+def test_bn_running_update_matches_torch_float64(oracle_mod):
+    import torch
+    import torch.nn.functional as F
+
+    g = np.random.Generator(np.random.PCG64(32))
+    x = (g.standard_normal((5, 3, 4, 6)) * 1.5 + 2).astype(np.float32)
+    rm0 = g.standard_normal(3).astype(np.float32)
+    rv0 = g.uniform(0.5, 2.0, 3).astype(np.float32)
+    _, mean, var = oracle_mod.batch_norm_train(x, with_stats=True)
+    rm, rv = oracle_mod.bn_running_update(mean, var, 5 * 4 * 6, rm0, rv0, momentum=0.1)
+    trm = torch.from_numpy(rm0).double()
+    trv = torch.from_numpy(rv0).double()
+    F.batch_norm(torch.from_numpy(x).double(), trm, trv, training=True, momentum=0.1, eps=1e-5)
+    np.testing.assert_allclose(rm, trm.numpy(), rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(rv, trv.numpy(), rtol=1e-6, atol=1e-7)
+
+
+def test_bn_running_update_closed_form(oracle_mod):
+    # values b +- a over an even count: batch mean b, biased var a^2, unbiased a^2 n/(n-1)
+    rm, rv = oracle_mod.bn_running_update([3.0], [4.0], 10, [1.0], [2.0], momentum=0.25)
+    assert abs(rm[0] - (0.75 * 1.0 + 0.25 * 3.0)) < 1e-7
+    assert abs(rv[0] - (0.75 * 2.0 + 0.25 * 4.0 * 10 / 9)) < 1e-6
+
+
 # ------------------------------------------------------------------------------------------
 # Conv -> normalize -> epilogue chains
 # ------------------------------------------------------------------------------------------
@@ -370,3 +394,37 @@ def test_chain_invariants(oracle_mod):
     var = s.reshape(2, -1).var(axis=1).reshape(2, 1, 1, 1, 1)
     ref = float(m[0]) * np.clip((s - mu) / np.sqrt(var + 1e-5), -1, 1)
     np.testing.assert_allclose(o1, ref[:, 0], rtol=0, atol=2e-7)
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+def test_conv_bn_eval_matches_torch_float64(oracle_mod, dims):
+    import torch
+    import torch.nn.functional as F
+
+    g = np.random.Generator(np.random.PCG64(51 + dims))
+    sp = (5, 8, 9) if dims == 3 else (10, 12)
+    x = g.standard_normal((2, 3) + sp).astype(np.float32)
+    w = (g.standard_normal((6, 3) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(6).astype(np.float32)
+    rm = g.standard_normal(6).astype(np.float32)
+    rv = g.uniform(0.2, 3.0, 6).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, 6).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, 6).astype(np.float32)
+    out = oracle_mod.conv_bn_eval(x, w, b, rm, rv, gamma=gm, beta=bt, scale=2.0)
+    t = lambda a: torch.from_numpy(a).double()
+    conv = F.conv3d if dims == 3 else F.conv2d
+    ref = 2.0 * F.batch_norm(conv(t(x), t(w), t(b)), t(rm), t(rv), t(gm), t(bt), training=False,
+                             eps=1e-5)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=2e-6)
+
+
+def test_conv_bn_eval_identity_statistics(oracle_mod):
+    # running mean 0, running var 1 - eps, gamma 1, beta 0, scale 1: the conv itself
+    g = np.random.Generator(np.random.PCG64(53))
+    x = g.standard_normal((1, 2, 6, 7)).astype(np.float32)
+    w = g.standard_normal((3, 2, 3, 3)).astype(np.float32)
+    b = g.standard_normal(3).astype(np.float32)
+    rv = np.full(3, 1.0 - 1e-5, np.float32)
+    out = oracle_mod.conv_bn_eval(x, w, b, np.zeros(3, np.float32), rv)
+    ref = oracle_mod.conv_k3(x, w, b) / np.sqrt(rv.astype(np.float64)[None, :, None, None] + 1e-5)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6)

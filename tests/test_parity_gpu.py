@@ -338,6 +338,38 @@ def test_bn_train(dev, nra, orc, shape):
     assert torch.equal(xt, y)
 
 
+# running statistics: resident single-workgroup, pipelined, split (S % 4 != 0) and the
+# beyond-index-range split path; two steps in a row so the update compounds
+BN_RUNNING_SHAPES = [(128, 64, 3844), (5, 2, 7), (2, 4, 4100), (33, 2, 16000), (65, 2, 32768)]
+
+
+def _check_running(rm_gpu, rv_gpu, rm_ref, rv_ref, what):
+    em = float(np.max(np.abs(H(rm_gpu) - rm_ref)))
+    ev = float(np.max(np.abs(H(rv_gpu) - rv_ref) / np.maximum(np.abs(rv_ref), 1e-30)))
+    _log("%s: running_mean max_abs_err %.3e, running_var max_rel_err %.3e" % (what, em, ev))
+    assert em <= 1e-5
+    assert ev <= 1e-5
+
+
+@pytest.mark.parametrize("shape", BN_RUNNING_SHAPES)
+def test_bn_running_statistics(dev, nra, orc, shape):
+    N, C, S = shape
+    g = np.random.Generator(np.random.PCG64(N * 7919 + C * 31 + S))
+    z = g.standard_normal(shape).astype(np.float32)
+    x = (z * g.uniform(0.1, 3, (1, C, 1)) + g.uniform(-5, 5, (1, C, 1))).astype(np.float32)
+    rm0 = g.uniform(-1, 1, C).astype(np.float32)
+    rv0 = g.uniform(0.5, 2, C).astype(np.float32)
+    rm, rv = T(rm0, dev), T(rv0, dev)
+    xt = T(x, dev)
+    _, mean, var = orc.batch_norm_train(x, with_stats=True)
+    rm_ref, rv_ref = rm0, rv0
+    for step in range(2):
+        y = nra.bn_train_forward(xt, running_mean=rm, running_var=rv, momentum=0.3)
+        rm_ref, rv_ref = orc.bn_running_update(mean, var, N * S, rm_ref, rv_ref, momentum=0.3)
+        _check_running(rm, rv, rm_ref, rv_ref, "bn_train %s step %d" % (shape, step))
+    assert maxerr(H(y), orc.batch_norm_train(x)) <= TOL
+
+
 # ------------------------------------------------------------------------------------------
 # Conv -> normalize -> epilogue
 # ------------------------------------------------------------------------------------------
@@ -420,6 +452,70 @@ def test_conv_chain_general(dev, nra, orc, shape, cout, batch, red, full):
     err = maxerr(H(out), ref)
     _log("chain %s Cout %d batch %s max_c %s: max_abs_err %.3e" % (shape, cout, batch, red, err))
     assert err <= TOL
+
+
+CHAIN_RUNNING_CASES = [
+    # (x shape, Cout, reduce_max_c): split path, pipelined in place, one workgroup per channel,
+    # max over channels, and the 2-D matrix-core producer shape
+    ((2, 8, 15, 13), 64, False), ((40, 2, 42, 42), 4, False), ((9, 2, 40, 42), 6, False),
+    ((3, 1, 5, 6, 7), 20, True), ((3, 8, 20, 22), 64, False),
+]
+
+
+@pytest.mark.parametrize("shape,cout,red", CHAIN_RUNNING_CASES)
+def test_conv_chain_running_statistics(dev, nra, orc, shape, cout, red):
+    g = np.random.Generator(np.random.PCG64(len(shape) * 1000 + cout * 3 + shape[0]))
+    x = g.standard_normal(shape).astype(np.float32)
+    dims = len(shape) - 2
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32)
+    pm = g.uniform(0.5, 2, cout).astype(np.float32)
+    rm0 = g.uniform(-1, 1, cout).astype(np.float32)
+    rv0 = g.uniform(0.5, 2, cout).astype(np.float32)
+    t = lambda a: T(a, dev)
+    rm, rv = t(rm0), t(rv0)
+    out = nra.conv_norm_epilogue_forward(t(x), t(w), t(b), norm=nra.NR_NORM_BATCH_TRAIN,
+                                         pre_mul=t(pm), reduce_max_c=red, running_mean=rm,
+                                         running_var=rv, momentum=0.25)
+    # the statistics are those of the normalized input: conv + bias, times pre_mul
+    c = orc.conv_k3(x, w, b) * pm.astype(np.float64).reshape((1, cout) + (1,) * dims)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    count = c.size // cout
+    rm_ref, rv_ref = orc.bn_running_update(mean, var, count, rm0, rv0, momentum=0.25)
+    _check_running(rm, rv, rm_ref, rv_ref, "chain %s Cout %d max_c %s" % (shape, cout, red))
+    ref = orc.conv_norm_epilogue(x, w, b, batch=True, pre_mul=pm, reduce_max_c=red)
+    assert maxerr(H(out), ref) <= TOL
+
+
+# eval-mode batch norm folded into the conv: the two model shapes, plus ragged small cases
+CONV_EVAL_CASES = [((128, 8, 64, 64), 64), ((128, 3, 16, 32, 32), 16), ((2, 3, 9, 11), 5),
+                   ((3, 2, 5, 6, 7), 17), ((1, 8, 15, 13), 64)]
+
+
+@pytest.mark.parametrize("shape,cout", CONV_EVAL_CASES)
+def test_conv_bn_eval(dev, nra, orc, shape, cout):
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(cout * 77 + len(shape)))
+    x = g.standard_normal(shape).astype(np.float32)
+    dims = len(shape) - 2
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32)
+    rm = g.uniform(-1, 1, cout).astype(np.float32)
+    rv = g.uniform(0.3, 3, cout).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, cout).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, cout).astype(np.float32)
+    t = lambda a: T(a, dev)
+    out = nra.conv_bn_eval_forward(t(x), t(w), t(b), t(rm), t(rv), gamma=t(gm), beta=t(bt),
+                                   out_scale=2.0)
+    ref = orc.conv_bn_eval(x, w, b, rm, rv, gamma=gm, beta=bt, scale=2.0)
+    err = maxerr(H(out), ref)
+    _log("conv_bn_eval %s Cout %d: max_abs_err %.3e" % (shape, cout, err))
+    assert err <= TOL
+    out2 = nra.conv_bn_eval_forward(t(x), t(w), None, t(rm), t(rv))  # no bias, no affine
+    assert maxerr(H(out2), orc.conv_bn_eval(x, w, None, rm, rv)) <= TOL
+    assert torch.equal(out, nra.conv_bn_eval_forward(t(x), t(w), t(b), t(rm), t(rv), gamma=t(gm),
+                                                     beta=t(bt), out_scale=2.0))
 
 
 def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
