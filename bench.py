@@ -63,6 +63,56 @@ def committed_traffic():
     return t.get("hbm_bytes_per_launch"), "from %s" % os.path.relpath(TRAFFIC_FILE, ROOT)
 
 
+HEADLINE_KERNEL = "norm_pipelined_kernel<256, 16, false, false>"
+COPY_KERNEL = "copy_vec_kernel"
+
+
+def _counter_rows(path, counter, needle):
+    import csv
+
+    with open(path, newline="") as f:
+        rows = [r for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter and needle in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [float(r["Counter_Value"]) for r in rows]
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Host-only: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE;
+    csv output) into the per-launch HBM byte count of the headline kernel. Each counter is
+    calibrated by what it reads for the plain copy kernel of the same run, which moves exactly
+    MIN_BYTES / 2 each way."""
+    kf = _counter_rows(fetch_csv, "FETCH_SIZE", HEADLINE_KERNEL)
+    kw = _counter_rows(write_csv, "WRITE_SIZE", HEADLINE_KERNEL)
+    cf = _counter_rows(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
+    cw = _counter_rows(write_csv, "WRITE_SIZE", COPY_KERNEL)
+    if not (kf and kw and cf and cw):
+        raise SystemExit("counter files lack the headline or the copy kernel")
+    mean = lambda v: sum(v) / len(v)
+    each_way = MIN_BYTES // 2
+    fs = each_way / (mean(cf) * 1024)
+    ws = each_way / (mean(cw) * 1024)
+    rd = mean(kf) * 1024 * fs
+    wr = mean(kw) * 1024 * ws
+    t = {
+        "kernel": HEADLINE_KERNEL,
+        "workload": "InstanceNorm2d x[112,64,512,512] fp32",
+        "fetch_size_kib_per_launch": kf, "write_size_kib_per_launch": kw,
+        "copy_kernel_fetch_kib": cf, "copy_kernel_write_kib": cw,
+        "copy_bytes_each_way": each_way,
+        "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
+        "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+        "hbm_bytes_per_launch": int(rd + wr), "algorithmic_bytes_per_launch": MIN_BYTES,
+        "traffic_over_algorithmic": round((rd + wr) / MIN_BYTES, 5),
+        "kernel_source_files": KERNEL_SOURCES, "kernel_source_sha256": kernel_source_hash(),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(json.dumps(t, indent=1))
+    return 0
+
+
 def time_calls(fn, steps, warmup, torch):
     """Returns (total ms for `steps` calls, mean ms per call measured around each call)."""
     for _ in range(warmup):
@@ -164,6 +214,15 @@ def extras(torch, nra, x, y, steps, warmup):
     out["conv3d_in3d_clamp_maxc_128x3x16x32x32"] = {
         "ms": round(per, 4), "conv_TFLOPs_over_chain_time": round(2 * 128 * 16 * 12600 * 81 / (per / 1e3) / 1e12, 2)}
     log("conv3d+IN3d+clamp+max_c: %.4f ms" % per)
+
+    # eval-mode batch norm folded into the conv (running statistics of the training chain)
+    rm4 = torch.empty(64, device=dev).uniform_(-0.5, 0.5)
+    rv4 = torch.empty(64, device=dev).uniform_(0.5, 2.0)
+    fe = lambda: nra.conv_bn_eval_forward(*a4, rm4, rv4, out=o4, gamma=g4, beta=be4, out_scale=2.0)
+    tot, per, med = time_calls(fe, steps, warmup, torch)
+    out["conv2d_bn_eval_x2_128x8x64x64"] = {
+        "ms": round(per, 4), "conv_TFLOPs": round(2 * 128 * 64 * 62 * 62 * 72 / (per / 1e3) / 1e12, 2)}
+    log("conv2d+bn_eval(folded)+x2: %.4f ms" % per)
     return out
 
 
@@ -176,7 +235,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write the committed HBM traffic summary from two rocprofv3 "
+                         "--pmc counter_collection.csv files of this script, then exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.gpus != 1:
         print("bench.py measures one GPU only: instance norm shards over the batch with no "
               "communication, and no multi-GPU path is built (--gpus %d refused)" % args.gpus,
