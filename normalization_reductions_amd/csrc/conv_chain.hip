@@ -5,16 +5,23 @@
 // ow+kw] (cross-correlation, valid, stride 1). IN3d page (task l2_p79): the 3-D form adds a
 // depth tap; extents shrink by 2 along each axis.
 //
-// Mapping: one lane per output position, KB output channels per thread kept in registers.
-// Every lane of a workgroup needs the same weight at the same time, so weights are read with
-// wave-uniform addresses (scalar loads from the read-only weight buffer) and each loaded input
-// value feeds KB fused multiply-adds. Inputs come through the vector L1/L2 path; neighbouring
-// lanes share most of their taps.
+// Three producers, picked per shape by launch_conv_k3:
+//   * conv2d_c8_mfma32_kernel: 2-D, C_in 8 -> C_out 64, W 64 (the batch-norm model's shape) on
+//     32x32x2 fp32 matrix instructions, persistent workgroups over LDS-staged boxes of rows;
+//   * conv_k3_ring_kernel: 2-D C_in 8 -> 64 of other widths and 3-D C_in 3 -> 16 (the IN3d
+//     model's shape) on 16x16x4 fp32 matrix instructions, persistent workgroups rolling a
+//     4-slice LDS ring over rows or depth planes;
+//   * conv_k3_kernel: any other shape on the vector ALU, one lane per output position and KB
+//     output channels per thread in registers; weights are read with wave-uniform addresses and
+//     each loaded input value feeds KB fused multiply-adds.
 //
 // Chain: IN3d page, its step list and fused elementwise kernel (multiply, normalize, clamp,
 // multiply, max over channels, each output position looping over the channels whose planes
 // are read with coalesced accesses); BN page: normalize with batch statistics, affine, scale.
+#include <stdint.h>
 #include <stdlib.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -96,96 +103,303 @@ __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const f
 // n + 16*(m/4), register m%4. So lane l = r16 + 16q supplies A for position r16 and tap
 // 4s + q, B for channel r16 and tap 4s + q, and receives channel r16 at 4 consecutive positions
 // 4q..4q+3 -- one 16-byte store per (row tile, channel tile).
-// Each lane keeps its weight fragment (KS x NT values) and its tap offsets into x in VGPRs for
-// the whole wave; A is gathered from x (16 lanes read 16 consecutive positions of one tap).
+//
+// Persistent form. The output is a sequence of outer slices (output rows in 2-D, output depth
+// planes in 3-D), each cut into T tiles of 16 positions; the grid splits the N * OO * T tiles
+// into equal contiguous ranges, one per workgroup. Output slice o of batch item n reads input
+// slices o, o+1, o+2 of every input channel; a workgroup keeps those in a 4-slot LDS ring
+// (slot = input slice mod 4, layout [slot][channel][slice]) and, while it computes slice o,
+// loads input slice o+3 into registers and drops it into the free slot afterwards -- one new
+// input slice per step, its latency hidden behind the step's matrix work. Each wave keeps the
+// weights of one 16-channel tile for all K steps in VGPRs (B operands); A operands are LDS
+// gathers (16 lanes read 16 consecutive positions of one tap).
+//
+// Tiles of a slice start `shift` positions early, shift = (o * positions per slice) mod 4, so
+// every 4-position group a lane stores is 16-byte aligned in the output; positions outside the
+// slice are computed from a dummy address and dropped.
 // ---------------------------------------------------------------------------------------------
 typedef float mf4 __attribute__((ext_vector_type(4)));
 constexpr int kMfmaBlock = 256;  // 4 waves
 
-template <int DIMS, int KS, int NT, int MT, int TPW>
-__global__ __launch_bounds__(kMfmaBlock) void conv_k3_mfma_kernel(ConvGeom g, const float* __restrict__ x,
+template <int DIMS, int KS, int WAVES_N, int MT, int PF, bool VEC>
+__global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
+                                                                   const float* __restrict__ x,
                                                                    const float* __restrict__ w,
                                                                    const float* __restrict__ b,
                                                                    float* __restrict__ c)
 {
+    extern __shared__ float ring[];  // [4][Cin][inner_in]
     constexpr int KD = DIMS == 3 ? 3 : 1;
+    constexpr int WAVES_M = (kMfmaBlock / 64) / WAVES_N;
+    constexpr int NE = VEC ? PF : 4 * PF;  // elements (float4 or float) a thread moves per slice
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
-    const int K = (int)g.Cin * KD * 9;
-    const int plane = (int)(g.H * g.W);
-    const int vol = (int)(g.D * plane);
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    const int Cin = (int)g.Cin;
+    const int K = Cin * KD * 9;
+    const int W = (int)g.W;
+    const int OW = (int)g.OW;
+    const int slice_floats = Cin * rg.inner_in;  // one input slice of every channel
+    const int64_t cstride = (int64_t)rg.outer_in * rg.inner_in;
 
-    int koff[KS];
-    float bw[KS][NT];
+    // Element e of this thread is float (or float4) index i = e * 256 + tid of an input slice;
+    // src[e] is its offset from the slice's channel-0 start in x (-1: past the slice's end).
+    int src[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int i = (e * kMfmaBlock + (int)threadIdx.x) * (VEC ? 4 : 1);
+        const int ci = i / rg.inner_in;
+        src[e] = i < slice_floats ? (int)(ci * cstride) + (i - ci * rg.inner_in) : -1;
+    }
+    mf4 pf[PF];
+    // Load input slice j of batch item n (all channels) into registers / store it into its slot.
+    auto fetch = [&](int64_t n, int j) {
+        const float* xs = x + n * Cin * cstride + (int64_t)j * rg.inner_in;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if (src[e] < 0) continue;
+            if (VEC)
+                pf[e] = *reinterpret_cast<const mf4*>(xs + src[e]);
+            else
+                pf[e >> 2][e & 3] = xs[src[e]];
+        }
+    };
+    auto drop = [&](int j) {
+        float* dst = ring + (j & 3) * slice_floats + (int)threadIdx.x * (VEC ? 4 : 1);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if (src[e] < 0) continue;
+            if (VEC)
+                *reinterpret_cast<mf4*>(dst + 4 * e * kMfmaBlock) = pf[e];
+            else
+                dst[e * kMfmaBlock] = pf[e >> 2][e & 3];
+        }
+    };
+
+    // This lane's B fragment (channel ch, taps 4s + q): weight, outer tap a (kd in 3-D, kh in
+    // 2-D) and the offset of the tap inside one slot, packed as (a << 24) | offset.
+    const int ch = wn * 16 + r16;
+    int tap[KS];
+    float bw[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int k = 4 * s + q;
         const bool valid = k < K;
         const int ci = k / (KD * 9);
         const int rem = k - ci * (KD * 9);
-        const int kd = rem / 9, kh = (rem % 9) / 3, kw = rem % 3;
-        koff[s] = valid ? ci * vol + kd * plane + kh * (int)g.W + kw : 0;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bw[s][nt] = valid ? w[(int64_t)(nt * 16 + r16) * K + k] : 0.f;
+        int a, in_off;
+        if (DIMS == 3) {
+            a = rem / 9;
+            in_off = ((rem % 9) / 3) * W + rem % 3;
+        } else {
+            a = rem / 3;
+            in_off = rem % 3;
+        }
+        tap[s] = valid ? (a << 24) | (ci * rg.inner_in + in_off) : 0;
+        bw[s] = valid ? w[(int64_t)ch * K + k] : 0.f;
     }
-    float bias[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bias[nt] = b ? b[nt * 16 + r16] : 0.f;
+    const float bias = b ? b[ch] : 0.f;
 
-    const int64_t n = blockIdx.y;
-    const float* xn = x + n * g.Cin * (int64_t)vol;
-    const int ohw = (int)(g.OH * g.OW);
-    const bool vec_ok = (g.SP & 3) == 0;
-
-    for (int t = 0; t < TPW; ++t) {
-        const int64_t tile0 = (((int64_t)blockIdx.x * TPW + t) * (kMfmaBlock / 64) + wave) * (MT * 16);
-        if (tile0 >= g.SP) break;
-        int pbase[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t m = tile0 + mt * 16 + r16;
-            int od = 0, oh = 0, ow = 0;
-            if (m < g.SP) {
-                const int mm = (int)m;
-                od = DIMS == 3 ? mm / ohw : 0;
-                const int r2 = mm - od * ohw;
-                oh = r2 / (int)g.OW;
-                ow = r2 - oh * (int)g.OW;
+    const int64_t total = (int64_t)g.N * rg.OO * rg.T;
+    const int64_t begin = total * blockIdx.x / gridDim.x;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    int64_t cur = -1;  // global slice (n * OO + o) whose window is in the ring
+    for (int64_t t = begin; t < end;) {
+        const int64_t sl = t / rg.T;
+        const int64_t n = sl / rg.OO;
+        const int o = (int)(sl - n * rg.OO);
+        const int tlo = (int)(t - sl * rg.T);
+        const int thi = (int)min((int64_t)rg.T, end - sl * rg.T);
+        if (sl != cur + 1 || o == 0) {  // new run: stage the whole window (synchronously)
+#pragma unroll 1
+            for (int j = o; j < o + 3; ++j) {
+                fetch(n, j);
+                drop(j);
             }
-            pbase[mt] = od * plane + oh * (int)g.W + ow;  // out-of-range rows read position 0
+            __syncthreads();
         }
-        mf4 acc[MT][NT];
+        const bool ahead = (sl + 1) * rg.T < end && o + 1 < rg.OO;  // next step continues this run
+        if (ahead) fetch(n, o + 3);
+
+        // slot offsets of this step's taps
+        int koff[KS];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int s = 0; s < KS; ++s)
+            koff[s] = ((o + (tap[s] >> 24)) & 3) * slice_floats + (tap[s] & 0xFFFFFF);
+        const int shift = rg.vec_out ? (int)(((int64_t)o * rg.inner_out) & 3) : 0;
+        float* cs = c + (n * g.Cout + ch) * g.SP + (int64_t)o * rg.inner_out;
+
+        for (int t0 = tlo + wm * MT; t0 < thi; t0 += WAVES_M * MT) {
+            int base[MT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mf4{bias[nt], bias[nt], bias[nt], bias[nt]};
+            for (int mt = 0; mt < MT; ++mt) {
+                int p = (t0 + mt) * 16 + r16 - shift;
+                p = (p >= 0 && p < rg.inner_out && t0 + mt < thi) ? p : 0;
+                if (DIMS == 3) {
+                    const int oh = p / OW;
+                    base[mt] = oh * W + (p - oh * OW);
+                } else {
+                    base[mt] = p;
+                }
+            }
+            mf4 acc[MT];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            float av[MT];
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mf4{bias, bias, bias, bias};
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) av[mt] = xn[pbase[mt] + koff[s]];
+            for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ring[base[mt] + koff[s]], bw[s],
+                                                                   acc[mt], 0, 0, 0);
+            }
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bw[s][nt], acc[mt][nt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t m0 = tile0 + mt * 16 + 4 * q;  // this lane's 4 positions
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                float* dst = c + (n * g.Cout + nt * 16 + r16) * g.SP + m0;
-                if (vec_ok && m0 + 3 < g.SP) {
-                    *reinterpret_cast<mf4*>(dst) = acc[mt][nt];
+            for (int mt = 0; mt < MT; ++mt) {
+                if (t0 + mt >= thi) continue;
+                const int p0 = (t0 + mt) * 16 + 4 * q - shift;  // this lane's 4 positions
+                if (rg.vec_out && p0 >= 0 && p0 + 3 < rg.inner_out) {
+                    *reinterpret_cast<mf4*>(cs + p0) = acc[mt];
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (m0 + r < g.SP) dst[r] = acc[mt][nt][r];
+                        if (p0 + r >= 0 && p0 + r < rg.inner_out) cs[p0 + r] = acc[mt][r];
                 }
             }
         }
+        if (ahead) drop(o + 3);
+        __syncthreads();
+        cur = sl;
+        t = (sl + 1) * rg.T;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2-D producer for C_in = 8, C_out = 64, W = 64 on v_mfma_f32_32x32x2f32 (the fp32 matrix
+// instruction that keeps the pipe busiest on gfx950: ~150 TFLOP/s measured with register
+// operands, against ~125-138 for 16x16x4). Lane l supplies A[m = l%32][k = l/32] (position m,
+// tap 2s + l/32) and B[k][n = l%32] (channel, tap); D[m][n] lands in lane n + 32*((m/4)%2),
+// register 4*(m/8) + m%4, so a lane stores channel l%32 at four aligned groups of 4 positions.
+//
+// A workgroup (4 waves) walks an equal contiguous range of boxes of B output rows of one batch
+// item (the last box of an item may be shorter). A box's positions are cut into tiles of 32
+// consecutive positions x all 64 channels, one tile per wave at a time; the two 32-channel
+// accumulators of a tile share every A operand. The B + 2 input rows x 8 channels a box reads
+// sit in LDS ([channel][row][64]), double-buffered: the next box's rows are loaded into
+// registers while the current box's matrix work runs. With the row width fixed at compile time
+// every tap's LDS offset is an immediate; a lane adds one of three per-tile bases (its
+// position, plus the distance from its lane-half's first tap to its second: 1, W - 2 or
+// B*W - 2).
+// ---------------------------------------------------------------------------------------------
+typedef float mf16 __attribute__((ext_vector_type(16)));
+constexpr int kC8Cin = 8, kC8Cout = 64, kC8K = 72, kC8Steps = 36, kC8W = 64;
+
+template <int B>
+__global__ __launch_bounds__(256) void conv2d_c8_mfma32_kernel(ConvGeom g,
+                                                               const float* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               const float* __restrict__ b,
+                                                               float* __restrict__ c)
+{
+    constexpr int W = kC8W, OW = W - 2;
+    constexpr int ROWS = B + 2;                   // input rows a box reads
+    constexpr int WIN = kC8Cin * ROWS * W;        // floats of one staged window
+    constexpr int NE = (WIN / 4 + 255) / 256;     // float4 a thread stages per window
+    constexpr int RUN4 = ROWS * W / 4;            // float4 per channel in a window
+    __shared__ float win[2 * WIN];
+    const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = l & 31, kk = l >> 5;
+    const int OH = (int)g.OH;
+    const int64_t HW = g.H * W;
+    const int nbox = (OH + B - 1) / B;
+
+    float bw[2][kC8Steps];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int s = 0; s < kC8Steps; ++s) bw[nt][s] = w[(nt * 32 + m) * kC8K + 2 * s + kk];
+    const float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
+
+    const int64_t total = g.N * (int64_t)nbox;
+    const int64_t begin = total * blockIdx.x / gridDim.x;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    mf4 pf[NE];
+    // input rows o0 .. o0 + nout + 1 of every channel; rows past the box's need are not loaded
+    auto fetch = [&](int64_t box) {
+        const int64_t n = box / nbox;
+        const int o0 = (int)(box - n * nbox) * B;
+        const int run4 = (min(B, OH - o0) + 2) * (W / 4);
+        const float* xs = x + n * kC8Cin * HW + (int64_t)o0 * W;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int i = e * 256 + (int)threadIdx.x;
+            const int ci = i / RUN4;
+            const int j = i - ci * RUN4;
+            if (i < kC8Cin * RUN4 && j < run4)
+                pf[e] = *reinterpret_cast<const mf4*>(xs + ci * HW + 4 * j);
+        }
+    };
+    auto drop = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int i = e * 256 + (int)threadIdx.x;
+            if (i < kC8Cin * RUN4) *reinterpret_cast<mf4*>(win + buf * WIN + 4 * i) = pf[e];
+        }
+    };
+
+    if (begin >= end) return;
+    fetch(begin);
+    drop(0);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t box = begin; box < end; ++box) {
+        const bool more = box + 1 < end;
+        if (more) fetch(box + 1);
+
+        const int64_t n = box / nbox;
+        const int o0 = (int)(box - n * nbox) * B;
+        const int BP = min(B, OH - o0) * OW;  // positions in this box
+        const int tiles = (BP + 31) / 32;
+        float* c0 = c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
+        float* c1 = c0 + 32 * g.SP;
+        for (int t = wave; t < tiles; t += 4) {
+            int p = 32 * t + m;
+            p = p < BP ? p : 0;
+            const int r = p / OW;
+            const float* a0 = win + buf * WIN + r * W + (p - r * OW);
+            const float* a1 = a0 + kk;                // second tap: next column
+            const float* a2 = a0 + kk * (W - 2);      // next row
+            const float* a3 = a0 + kk * (B * W - 2);  // next channel
+            mf16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int s = 0; s < kC8Steps; ++s) {
+                const int k0 = 2 * s;  // tap of lanes 0..31; lanes 32..63 take k0 + 1
+                const int ci = k0 / 9, kh = (k0 % 9) / 3, kw = k0 % 3;
+                const int off = ci * ROWS * W + kh * W + kw;
+                const float av = kw < 2 ? a1[off] : kh < 2 ? a2[off] : a3[off];
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bw[0][s], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bw[1][s], acc1, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int p0 = 32 * t + 8 * j + 4 * kk;  // positions of registers 4j..4j+3
+                const mf4 v0 = mf4{acc0[4 * j], acc0[4 * j + 1], acc0[4 * j + 2], acc0[4 * j + 3]} + bias0;
+                const mf4 v1 = mf4{acc1[4 * j], acc1[4 * j + 1], acc1[4 * j + 2], acc1[4 * j + 3]} + bias1;
+                if (p0 + 3 < BP) {
+                    *reinterpret_cast<mf4*>(c0 + p0) = v0;
+                    *reinterpret_cast<mf4*>(c1 + p0) = v1;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (p0 + q < BP) {
+                            c0[p0 + q] = v0[q];
+                            c1[p0 + q] = v1[q];
+                        }
+                }
+            }
+        }
+        if (more) drop(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
     }
 }
 
@@ -288,34 +502,98 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_kernel(ChainArgs a)
 }  // namespace
 
 namespace {
-template <int DIMS, int KS, int NT, int MT, int TPW>
-hipError_t launch_mfma(const ConvGeom& g, const float* x, const float* w, const float* b, float* c,
-                       hipStream_t stream)
-{
-    const int64_t per_wg = (int64_t)TPW * (kMfmaBlock / 64) * MT * 16;
-    const dim3 grid((unsigned)((g.SP + per_wg - 1) / per_wg), (unsigned)g.N);
-    conv_k3_mfma_kernel<DIMS, KS, NT, MT, TPW><<<grid, dim3(kMfmaBlock), 0, stream>>>(g, x, w, b, c);
-    return hipGetLastError();
-}
-
 bool conv_valu_forced()
 {
     const char* e = getenv("NORMRED_CONV");
     return e && e[0] == 'v';  // "valu": the vector-ALU producer (comparisons)
+}
+
+constexpr int kRingLdsMax = 64 * 1024;  // LDS bytes of one workgroup's ring
+
+// Ring geometry for the persistent producer; false when the shape does not fit (ring beyond
+// kRingLdsMax, one input slice beyond PF float4 per thread, or offsets beyond 24 bits).
+bool make_ring(const ConvGeom& g, const float* x, const float* c, int PF, ConvRing* rg)
+{
+    const bool d3 = g.dims == 3;
+    rg->OO = (int)(d3 ? g.OD : g.OH);
+    rg->outer_in = (int)(d3 ? g.D : g.H);
+    rg->inner_in = (int)(d3 ? g.H * g.W : g.W);
+    rg->inner_out = (int)(d3 ? g.OH * g.OW : g.OW);
+    const int64_t slice = g.Cin * (int64_t)rg->inner_in;
+    if (4 * slice * (int64_t)sizeof(float) > kRingLdsMax) return false;
+    if (slice > 4LL * PF * kMfmaBlock || 4 * slice >= (1 << 24)) return false;
+    rg->vec_in = (rg->inner_in % 4 == 0) && ((uintptr_t)x % 16 == 0);
+    rg->vec_out = (g.SP % 4 == 0) && ((uintptr_t)c % 16 == 0);
+    // largest start shift of a slice's tiles: 0 when a slice is a multiple of 4 positions,
+    // 2 when it is even, else 3
+    const int maxshift = !rg->vec_out ? 0 : rg->inner_out % 4 == 0 ? 0 : rg->inner_out % 2 == 0 ? 2 : 3;
+    rg->T = (rg->inner_out + maxshift + 15) / 16;
+    return true;
+}
+
+int ring_grid(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            cus = 256;
+        else
+            cus = prop.multiProcessorCount;
+    }
+    if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs_per_cu = std::max(1, atoi(e));
+    const int64_t total = g.N * (int64_t)rg.OO * rg.T;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(total, (int64_t)cus * wgs_per_cu));
+}
+
+template <int DIMS, int KS, int WAVES_N, int MT, int PF>
+hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, const float* x,
+                       const float* w, const float* b, float* c, hipStream_t stream)
+{
+    const size_t lds = 4 * (size_t)g.Cin * rg.inner_in * sizeof(float);
+    const int grid = ring_grid(g, rg, wgs_per_cu);
+    if (rg.vec_in)
+        conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true>
+            <<<dim3(grid), dim3(kMfmaBlock), lds, stream>>>(g, rg, x, w, b, c);
+    else
+        conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false>
+            <<<dim3(grid), dim3(kMfmaBlock), lds, stream>>>(g, rg, x, w, b, c);
+    return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream)
 {
-    // Matrix-core producer for the compiled (dims, C_in, C_out) shapes; int32 offsets into one
+    // Matrix-core producers for the compiled (dims, C_in, C_out) shapes; int32 offsets into one
     // batch item of x.
     const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+    ConvRing rg;
     if (!conv_valu_forced() && small) {
-        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64)
-            return launch_mfma<2, 18, 4, 4, 4>(g, x, w, b, c, stream);
-        if (g.dims == 3 && g.Cin == 3 && g.Cout == 16)
-            return launch_mfma<3, 21, 1, 8, 4>(g, x, w, b, c, stream);
+        // 16-byte output stores need every box to start on a multiple of 4 positions: B * 62
+        // is, SP % 4 == 0 keeps planes aligned
+        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64 && g.W == kC8W && (uintptr_t)x % 16 == 0 &&
+            (uintptr_t)c % 16 == 0 && g.SP % 4 == 0) {
+            static int cus = 0;
+            if (cus == 0) {
+                int dev = 0;
+                hipDeviceProp_t prop;
+                cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+                          ? prop.multiProcessorCount : 256;
+            }
+            int wgs = 2;  // per CU: one wave per SIMD each, the most its VGPR use allows
+            if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs = std::max(1, atoi(e));
+            constexpr int B = 4;  // output rows per box (2 rows measured ~8 % slower)
+            const int64_t nbox = (g.OH + B - 1) / B;
+            const int64_t grid = std::min<int64_t>(g.N * nbox, (int64_t)cus * wgs);
+            conv2d_c8_mfma32_kernel<B><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(g, x, w, b, c);
+            return hipGetLastError();
+        }
+        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64 && make_ring(g, x, c, 1, &rg))
+            return launch_ring<2, 18, 4, 4, 1>(g, rg, 4, x, w, b, c, stream);
+        if (g.dims == 3 && g.Cin == 3 && g.Cout == 16 && make_ring(g, x, c, 3, &rg))
+            return launch_ring<3, 21, 1, 2, 3>(g, rg, 3, x, w, b, c, stream);
     }
     const dim3 grid((unsigned)((g.SP + kConvBlock - 1) / kConvBlock), (unsigned)g.N,
                     (unsigned)((g.Cout + kKB - 1) / kKB));

@@ -69,6 +69,18 @@ struct ConvGeom {
     int64_t OD, OH, OW, SP;    // output extent, SP = OD*OH*OW
 };
 
+// Geometry of the persistent conv producer: the output as N * OO outer slices (rows in 2-D,
+// depth planes in 3-D) of T tiles of 16 positions each.
+struct ConvRing {
+    int OO;         // outer output slices per batch item (OH or OD)
+    int outer_in;   // H or D
+    int inner_in;   // W or H*W: floats per input slice of one channel
+    int inner_out;  // OW or OH*OW: positions per output slice
+    int T;          // tiles per output slice (including the alignment shift)
+    int vec_in;     // 16-byte input loads
+    int vec_out;    // 16-byte output stores (aligned groups of 4 positions)
+};
+
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream);
 

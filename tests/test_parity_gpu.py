@@ -425,6 +425,12 @@ CHAIN_CASES = [
     ((3, 8, 20, 22), 64, True, False, True),     # 360 positions: 16-byte stores, in place
     ((2, 3, 6, 9, 11), 16, False, True, True),   # 252 positions, max over channels
     ((2, 3, 5, 7, 8), 16, False, True, True),    # 90 positions: scalar stores
+    # the 2-D 64-wide producer (32-position tiles taken from a counter): one row, odd heights
+    # (rows starting at position 2 mod 4), split path, max over channels
+    ((1, 8, 3, 64), 64, True, False, True),
+    ((3, 8, 9, 64), 64, True, False, True),
+    ((5, 8, 17, 64), 64, False, False, True),
+    ((2, 8, 6, 64), 64, True, True, True),
 ]
 
 
@@ -489,7 +495,7 @@ def test_conv_chain_running_statistics(dev, nra, orc, shape, cout, red):
 
 # eval-mode batch norm folded into the conv: the two model shapes, plus ragged small cases
 CONV_EVAL_CASES = [((128, 8, 64, 64), 64), ((128, 3, 16, 32, 32), 16), ((2, 3, 9, 11), 5),
-                   ((3, 2, 5, 6, 7), 17), ((1, 8, 15, 13), 64)]
+                   ((3, 2, 5, 6, 7), 17), ((1, 8, 15, 13), 64), ((7, 8, 13, 64), 64)]
 
 
 @pytest.mark.parametrize("shape,cout", CONV_EVAL_CASES)
