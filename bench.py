@@ -243,6 +243,17 @@ def extras(torch, nra, x, y, steps, warmup):
         "ms": round(per, 4), "conv_TFLOPs_over_chain_time": round(2 * 128 * 16 * 12600 * 81 / (per / 1e3) / 1e12, 2)}
     log("conv3d+IN3d+clamp+max_c: %.4f ms" % per)
 
+    # the same IN3d chain with channels-last input and conv output
+    x5cl = a5[0].permute(0, 2, 3, 4, 1).contiguous()
+    f5cl = lambda: nra.conv_norm_epilogue_forward(x5cl, a5[1], a5[2], out=o5,
+                                                  norm=nra.NR_NORM_INSTANCE, pre_mul=m5,
+                                                  clamp=(-1.0, 1.0), post_mul=m5,
+                                                  reduce_max_c=True, channels_last=True)
+    tot, per, med = time_calls(f5cl, steps, warmup, torch, flush)
+    out["conv3d_in3d_clamp_maxc_channels_last_128x16x32x32x3"] = {
+        "ms": round(per, 4), "conv_TFLOPs_over_chain_time": round(2 * 128 * 16 * 12600 * 81 / (per / 1e3) / 1e12, 2)}
+    log("conv3d+IN3d+clamp+max_c, channels last: %.4f ms" % per)
+
     # eval-mode batch norm folded into the conv (running statistics of the training chain)
     rm4 = torch.empty(64, device=dev).uniform_(-0.5, 0.5)
     rv4 = torch.empty(64, device=dev).uniform_(0.5, 2.0)

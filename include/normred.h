@@ -155,6 +155,13 @@ nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, in
  * groups fit the read-once kernels), the conv writes straight into `out`, which is then
  * normalized in place: `out` must be 16-byte aligned (else NR_ERR_MISALIGNED) and the workspace
  * holds only exchange slots. Otherwise the conv output is staged in the workspace.
+ *
+ * Channels last (channels_last = 1; IN3d page, its note on an (N, spatial, C) layout that makes
+ * the max over channels contiguous): x is [N, (D,) H, W, C_in] and out is
+ * [N, (D-2,) H-2, W-2, C_out], or [N, (D-2,) H-2, W-2] with reduce_max_c; w keeps its layout.
+ * The arithmetic and the step order are the same. C_out <= 256 (else NR_ERR_UNSUPPORTED). The
+ * statistics take a two-pass path over the conv output (staged in the workspace when
+ * reduce_max_c, else written to `out` and normalized in place); no alignment is required.
  * ------------------------------------------------------------------------------------------ */
 #define NR_NORM_BATCH_TRAIN 1
 #define NR_NORM_INSTANCE 2
@@ -177,6 +184,7 @@ typedef struct nr_conv_norm_desc {
     float momentum;              /* running-statistics update (NR_NORM_BATCH_TRAIN only), */
     float* running_mean;         /* as in bn_train_forward_ex: [C_out] each, both or neither */
     float* running_var;
+    int32_t channels_last;       /* 0: x, out planar (N, C, spatial); 1: (N, spatial, C) */
 } nr_conv_norm_desc;
 
 /* 0 if the descriptor is invalid. */
@@ -200,8 +208,9 @@ nr_status conv_norm_epilogue_forward(const nr_conv_norm_desc* d, const float* x,
  *    clamp, reduce_max_c and the running-statistics update fields must be unset
  *    (NR_ERR_UNSUPPORTED otherwise).
  * running_mean, running_var: [C_out] device buffers (read only).
- * out: [N, C_out, (D-2,) H-2, W-2]. workspace: >= conv_bn_eval_workspace_size(d) bytes (holds
- *    the folded weights; refilled by every call).
+ * out: [N, C_out, (D-2,) H-2, W-2], or [N, (D-2,) H-2, W-2, C_out] with d->channels_last (x
+ *    then [N, (D,) H, W, C_in]). workspace: >= conv_bn_eval_workspace_size(d) bytes (holds the
+ *    folded weights; refilled by every call).
  * ------------------------------------------------------------------------------------------ */
 size_t conv_bn_eval_workspace_size(const nr_conv_norm_desc* d);
 

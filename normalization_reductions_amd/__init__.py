@@ -184,17 +184,20 @@ def bn_train_forward(x, y=None, *, eps: float = 1e-5, gamma=None, beta=None,
 # Conv -> normalize -> epilogue
 # ---------------------------------------------------------------------------------------------
 def _desc(x, w, *, norm, eps, pre_mul, gamma, beta, out_scale, clamp, post_mul, reduce_max_c,
-          running_mean=None, running_var=None, momentum=0.1):
+          running_mean=None, running_var=None, momentum=0.1, channels_last=False):
     dims = x.dim() - 2
     if dims not in (2, 3):
-        raise ValueError("x must be [N, C, H, W] or [N, C, D, H, W]")
-    if w.dim() != x.dim() or int(w.shape[1]) != int(x.shape[1]):
+        raise ValueError("x must be [N, C, H, W] or [N, C, D, H, W] (channels last: "
+                         "[N, H, W, C] or [N, D, H, W, C])")
+    cin = int(x.shape[-1]) if channels_last else int(x.shape[1])
+    if w.dim() != x.dim() or int(w.shape[1]) != cin:
         raise ValueError("w must be [C_out, C_in, 3, ...] matching x")
     d = _lib.ConvNormDesc()
     d.spatial_dims = dims
     d.ksize = int(w.shape[-1])
-    d.N, d.C_in, d.C_out = int(x.shape[0]), int(x.shape[1]), int(w.shape[0])
-    sp = [int(s) for s in x.shape[2:]]
+    d.N, d.C_in, d.C_out = int(x.shape[0]), cin, int(w.shape[0])
+    d.channels_last = 1 if channels_last else 0
+    sp = [int(s) for s in (x.shape[1:-1] if channels_last else x.shape[2:])]
     d.in_d, d.in_h, d.in_w = (sp[0], sp[1], sp[2]) if dims == 3 else (1, sp[0], sp[1])
     d.norm = norm
     d.eps = float(eps)
@@ -211,7 +214,10 @@ def _desc(x, w, *, norm, eps, pre_mul, gamma, beta, out_scale, clamp, post_mul, 
     d.running_mean = _opt_ptr(running_mean, "running_mean", cout, x.device)
     d.running_var = _opt_ptr(running_var, "running_var", cout, x.device)
     osp = tuple(s - 2 for s in sp)
-    oshape = (d.N,) + osp if reduce_max_c else (d.N, cout) + osp
+    if reduce_max_c:
+        oshape = (d.N,) + osp
+    else:
+        oshape = (d.N,) + osp + (cout,) if channels_last else (d.N, cout) + osp
     return d, oshape
 
 
@@ -222,9 +228,11 @@ def conv_norm_epilogue_workspace_size(desc) -> int:
 def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRAIN, eps=1e-5,
                                pre_mul=None, gamma=None, beta=None, out_scale=1.0, clamp=None,
                                post_mul=None, reduce_max_c=False, running_mean=None,
-                               running_var=None, momentum=0.1, workspace=None, stream=None):
+                               running_var=None, momentum=0.1, channels_last=False,
+                               workspace=None, stream=None):
     """k=3 valid conv (+bias) -> pre_mul -> batch/instance norm -> gamma, beta -> out_scale ->
-    clamp -> post_mul -> optional max over channels (see normred.h)."""
+    clamp -> post_mul -> optional max over channels (see normred.h). channels_last: x is
+    [N, (D,) H, W, C_in] and the output [N, (D-2,) H-2, W-2, C_out] (or the channel max)."""
     lib = _lib.load()
     torch = _torch()
     _dev_f32(x, "x")
@@ -232,7 +240,7 @@ def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRA
     d, oshape = _desc(x, w, norm=norm, eps=eps, pre_mul=pre_mul, gamma=gamma, beta=beta,
                       out_scale=out_scale, clamp=clamp, post_mul=post_mul,
                       reduce_max_c=reduce_max_c, running_mean=running_mean,
-                      running_var=running_var, momentum=momentum)
+                      running_var=running_var, momentum=momentum, channels_last=channels_last)
     bp = _opt_ptr(b, "b", d.C_out, x.device)
     if out is None:
         out = torch.empty(oshape, dtype=torch.float32, device=x.device)
@@ -254,7 +262,8 @@ def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRA
 
 
 def conv_bn_eval_forward(x, w, b, running_mean, running_var, out=None, *, eps=1e-5, gamma=None,
-                         beta=None, out_scale=1.0, workspace=None, stream=None):
+                         beta=None, out_scale=1.0, channels_last=False, workspace=None,
+                         stream=None):
     """k=3 valid conv (+bias) -> eval-mode batch norm with running statistics -> * out_scale,
     folded into the conv weights (see normred.h)."""
     lib = _lib.load()
@@ -262,7 +271,8 @@ def conv_bn_eval_forward(x, w, b, running_mean, running_var, out=None, *, eps=1e
     _dev_f32(x, "x")
     _dev_f32(w, "w")
     d, oshape = _desc(x, w, norm=NR_NORM_BATCH_TRAIN, eps=eps, pre_mul=None, gamma=gamma, beta=beta,
-                      out_scale=out_scale, clamp=None, post_mul=None, reduce_max_c=False)
+                      out_scale=out_scale, clamp=None, post_mul=None, reduce_max_c=False,
+                      channels_last=channels_last)
     bp = _opt_ptr(b, "b", d.C_out, x.device)
     rm = _opt_ptr(running_mean, "running_mean", d.C_out, x.device)
     rv = _opt_ptr(running_var, "running_var", d.C_out, x.device)

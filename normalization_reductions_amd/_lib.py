@@ -54,6 +54,7 @@ class ConvNormDesc(ctypes.Structure):
         ("momentum", ctypes.c_float),
         ("running_mean", ctypes.c_void_p),
         ("running_var", ctypes.c_void_p),
+        ("channels_last", ctypes.c_int32),
     ]
 
 

@@ -313,6 +313,11 @@ nr_status check_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
     c.SP = sp;
     if (c.N > 65535 || (c.Cout + 15) / 16 > 65535 || (sp + 255) / 256 > 0x7fffffffLL)
         return fail(NR_ERR_UNSUPPORTED, "%s: shape exceeds the launch grid limits", fn);
+    if (d->channels_last != 0 && d->channels_last != 1)
+        return fail(NR_ERR_INVALID_ARG, "%s: channels_last must be 0 or 1", fn);
+    c.cl = d->channels_last;
+    if (c.cl && c.Cout > 256)
+        return fail(NR_ERR_UNSUPPORTED, "%s: channels_last supports C_out <= 256", fn);
     *g = c;
     return NR_OK;
 }
@@ -323,6 +328,7 @@ struct ChainLayout {
     size_t exch = 0;
     size_t cbuf = 0, partials = 0, stats = 0, bytes = 0;
     SplitGeom sg;
+    ClGeom cg;              // channels last
 };
 
 // Two plans. Without the max over channels and with S % 4 == 0 the conv writes its output
@@ -334,6 +340,21 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
     ChainLayout L;
     size_t off = kHeaderBytes;
     const int64_t groups = batch ? g.Cout : g.N * g.Cout;
+    if (g.cl) {
+        // channels last: conv output staged only for the max over channels (else written to
+        // `out` and normalized in place), partials per (n, chunk, k), group statistics
+        L.cg = cl_geometry(g.N, g.Cout, g.SP, batch);
+        if (reduce_max_c) {
+            L.cbuf = off;
+            off = align_up(off + (size_t)(g.N * g.Cout * g.SP) * sizeof(float), kWsAlign);
+        }
+        L.partials = off;
+        off = align_up(off + cl_partials_bytes(L.cg), kWsAlign);
+        L.stats = off;
+        off = align_up(off + (size_t)groups * sizeof(GroupStat), kWsAlign);
+        L.bytes = off;
+        return L;
+    }
     const int64_t len = batch ? g.N * g.SP : g.SP;
     if (!reduce_max_c && g.SP % 4 == 0 && choose_resident(len, batch, true, &L.cfg_idx, &L.P) &&
         groups * L.P <= 0xF0000000LL && groups <= 0x7fffffffLL) {
@@ -524,6 +545,38 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     const bool batch = d->norm == NR_NORM_BATCH_TRAIN;
     const ChainLayout L = chain_layout(g, batch, d->reduce_max_c != 0);
     if ((s = check_workspace(workspace, workspace_bytes, L.bytes, fn)) != NR_OK) return s;
+    if (g.cl) {
+        if (L.cg.N * L.cg.chunks > 0x7fffffffLL || L.cg.chunks > 0x7fffffffLL)
+            return fail(NR_ERR_UNSUPPORTED, "%s: too many statistics chunks for one launch", fn);
+        float* c = d->reduce_max_c ? ws_at<float>(workspace, L.cbuf) : out;
+        hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
+        e = launch_cl_stats(L.cg, c, d->pre_mul, ws_at<float4>(workspace, L.partials), d->eps,
+                            stats, RunningStats{d->running_mean, d->running_var, d->momentum},
+                            stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        ChainArgs a;
+        a.c = c;
+        a.out = out;
+        a.N = g.N;
+        a.Cout = g.Cout;
+        a.SP = g.SP;
+        a.batch = batch;
+        a.stats = stats;
+        a.pre_mul = d->pre_mul;
+        a.gamma = d->gamma;
+        a.beta = d->beta;
+        a.out_scale = d->out_scale;
+        a.clamp = d->clamp;
+        a.lo = d->clamp_lo;
+        a.hi = d->clamp_hi;
+        a.post_mul = d->post_mul;
+        a.reduce_max_c = d->reduce_max_c;
+        e = launch_cl_apply(a, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     if (L.resident) {
         if (!aligned(out, 16))
             return fail(NR_ERR_MISALIGNED, "%s: out must be 16-byte aligned for this shape", fn);

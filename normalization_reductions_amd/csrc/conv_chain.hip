@@ -32,7 +32,7 @@ namespace {
 constexpr int kConvBlock = 256;
 constexpr int kKB = 16;  // output channels per thread
 
-template <int DIMS, bool FULL>
+template <int DIMS, bool FULL, bool CL>
 __device__ __forceinline__ void conv_point(const ConvGeom& g, const float* __restrict__ x,
                                            const float* __restrict__ w,
                                            const float* __restrict__ b, float* __restrict__ c,
@@ -56,7 +56,9 @@ __device__ __forceinline__ void conv_point(const ConvGeom& g, const float* __res
     for (int k = 0; k < kKB; ++k) acc[k] = (k < kcount && b) ? b[k0 + k] : 0.f;
 
     for (int64_t ci = 0; ci < g.Cin; ++ci) {
-        const float* xp = x + (((n * g.Cin + ci) * g.D + od) * g.H + oh) * g.W + ow;
+        const float* xp = CL ? x + (((n * g.D + od) * g.H + oh) * g.W + ow) * g.Cin + ci
+                             : x + (((n * g.Cin + ci) * g.D + od) * g.H + oh) * g.W + ow;
+        const int64_t xs = CL ? g.Cin : 1;  // stride between neighbouring positions of x
         const float* wp = w + ((k0 * g.Cin + ci) * KD) * 9;
         const int64_t wk = g.Cin * KD * 9;  // stride between output channels in w
 #pragma unroll
@@ -65,7 +67,7 @@ __device__ __forceinline__ void conv_point(const ConvGeom& g, const float* __res
             for (int kh = 0; kh < 3; ++kh) {
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) {
-                    const float xv = xp[(kd * g.H + kh) * g.W + kw];
+                    const float xv = xp[((kd * g.H + kh) * g.W + kw) * xs];
                     const int t = (kd * 3 + kh) * 3 + kw;
 #pragma unroll
                     for (int k = 0; k < kKB; ++k)
@@ -76,10 +78,15 @@ __device__ __forceinline__ void conv_point(const ConvGeom& g, const float* __res
     }
 #pragma unroll
     for (int k = 0; k < kKB; ++k)
-        if (k < kcount) c[(n * g.Cout + k0 + k) * g.SP + i] = acc[k];
+        if (k < kcount) {
+            if (CL)
+                c[(n * g.SP + i) * g.Cout + k0 + k] = acc[k];
+            else
+                c[(n * g.Cout + k0 + k) * g.SP + i] = acc[k];
+        }
 }
 
-template <int DIMS>
+template <int DIMS, bool CL>
 __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const float* __restrict__ x,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ b,
@@ -90,9 +97,9 @@ __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const f
     const int64_t k0 = (int64_t)blockIdx.z * kKB;
     if (i >= g.SP) return;
     if (k0 + kKB <= g.Cout)
-        conv_point<DIMS, true>(g, x, w, b, c, n, k0, i);
+        conv_point<DIMS, true, CL>(g, x, w, b, c, n, k0, i);
     else
-        conv_point<DIMS, false>(g, x, w, b, c, n, k0, i);
+        conv_point<DIMS, false, CL>(g, x, w, b, c, n, k0, i);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -121,14 +128,14 @@ __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const f
 typedef float mf4 __attribute__((ext_vector_type(4)));
 constexpr int kMfmaBlock = 256;  // 4 waves
 
-template <int DIMS, int KS, int WAVES_N, int MT, int PF, bool VEC>
+template <int DIMS, int KS, int WAVES_N, int MT, int PF, bool VEC, bool CL>
 __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
                                                                    const float* __restrict__ x,
                                                                    const float* __restrict__ w,
                                                                    const float* __restrict__ b,
                                                                    float* __restrict__ c)
 {
-    extern __shared__ float ring[];  // [4][Cin][inner_in]
+    extern __shared__ float ring[];  // [4][Cin][inner_in], channels last: [4][inner_in][Cin]
     constexpr int KD = DIMS == 3 ? 3 : 1;
     constexpr int WAVES_M = (kMfmaBlock / 64) / WAVES_N;
     constexpr int NE = VEC ? PF : 4 * PF;  // elements (float4 or float) a thread moves per slice
@@ -144,18 +151,21 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
     const int64_t cstride = (int64_t)rg.outer_in * rg.inner_in;
 
     // Element e of this thread is float (or float4) index i = e * 256 + tid of an input slice;
-    // src[e] is its offset from the slice's channel-0 start in x (-1: past the slice's end).
+    // src[e] is its offset from the slice's start in x (-1: past the slice's end). Planar x
+    // holds a slice as Cin runs of inner_in floats cstride apart; channels-last x holds it as
+    // one contiguous run.
     int src[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int i = (e * kMfmaBlock + (int)threadIdx.x) * (VEC ? 4 : 1);
         const int ci = i / rg.inner_in;
-        src[e] = i < slice_floats ? (int)(ci * cstride) + (i - ci * rg.inner_in) : -1;
+        src[e] = i >= slice_floats ? -1 : CL ? i : (int)(ci * cstride) + (i - ci * rg.inner_in);
     }
     mf4 pf[PF];
     // Load input slice j of batch item n (all channels) into registers / store it into its slot.
     auto fetch = [&](int64_t n, int j) {
-        const float* xs = x + n * Cin * cstride + (int64_t)j * rg.inner_in;
+        const float* xs = CL ? x + (n * rg.outer_in + j) * (int64_t)slice_floats
+                             : x + n * Cin * cstride + (int64_t)j * rg.inner_in;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             if (src[e] < 0) continue;
@@ -196,10 +206,15 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
             a = rem / 3;
             in_off = rem % 3;
         }
-        tap[s] = valid ? (a << 24) | (ci * rg.inner_in + in_off) : 0;
+        const int lds_off = CL ? in_off * Cin + ci : ci * rg.inner_in + in_off;
+        tap[s] = valid ? (a << 24) | lds_off : 0;
         bw[s] = valid ? w[(int64_t)ch * K + k] : 0.f;
     }
-    const float bias = b ? b[ch] : 0.f;
+    // accumulator start: the bias of the channel(s) a lane's 4 results belong to (planar: its
+    // channel ch at 4 positions; channels last: channels 4q..4q+3 of its tile at one position)
+    mf4 bias4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias4[r] = b ? b[CL ? wn * 16 + 4 * q + r : ch] : 0.f;
 
     const int64_t total = (int64_t)g.N * rg.OO * rg.T;
     const int64_t begin = total * blockIdx.x / gridDim.x;
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             koff[s] = ((o + (tap[s] >> 24)) & 3) * slice_floats + (tap[s] & 0xFFFFFF);
-        const int shift = rg.vec_out ? (int)(((int64_t)o * rg.inner_out) & 3) : 0;
+        const int shift = (!CL && rg.vec_out) ? (int)(((int64_t)o * rg.inner_out) & 3) : 0;
         float* cs = c + (n * g.Cout + ch) * g.SP + (int64_t)o * rg.inner_out;
 
         for (int t0 = tlo + wm * MT; t0 < thi; t0 += WAVES_M * MT) {
@@ -242,20 +257,37 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
                 } else {
                     base[mt] = p;
                 }
+                if (CL) base[mt] *= Cin;
             }
             mf4 acc[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mf4{bias, bias, bias, bias};
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = bias4;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ring[base[mt] + koff[s]], bw[s],
-                                                                   acc[mt], 0, 0, 0);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float av = ring[base[mt] + koff[s]];
+                    // channels last: D = W x X, so a lane receives 4 consecutive channels of
+                    // one position (D[m][n] lands in lane n + 16*(m/4), register m%4)
+                    acc[mt] = CL ? __builtin_amdgcn_mfma_f32_16x16x4f32(bw[s], av, acc[mt], 0, 0, 0)
+                                 : __builtin_amdgcn_mfma_f32_16x16x4f32(av, bw[s], acc[mt], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if (t0 + mt >= thi) continue;
+                if (CL) {
+                    const int p = (t0 + mt) * 16 + r16;  // this lane's position
+                    if (p >= rg.inner_out) continue;
+                    float* dst = c + (n * g.SP + (int64_t)o * rg.inner_out + p) * g.Cout + wn * 16 + 4 * q;
+                    if (rg.vec_out) {
+                        *reinterpret_cast<mf4*>(dst) = acc[mt];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dst[r] = acc[mt][r];
+                    }
+                    continue;
+                }
                 const int p0 = (t0 + mt) * 16 + 4 * q - shift;  // this lane's 4 positions
                 if (rg.vec_out && p0 >= 0 && p0 + 3 < rg.inner_out) {
                     *reinterpret_cast<mf4*>(cs + p0) = acc[mt];
@@ -522,6 +554,13 @@ bool make_ring(const ConvGeom& g, const float* x, const float* c, int PF, ConvRi
     const int64_t slice = g.Cin * (int64_t)rg->inner_in;
     if (4 * slice * (int64_t)sizeof(float) > kRingLdsMax) return false;
     if (slice > 4LL * PF * kMfmaBlock || 4 * slice >= (1 << 24)) return false;
+    if (g.cl) {
+        // a slice is one contiguous run; a lane stores 4 consecutive channels of a position
+        rg->vec_in = (slice % 4 == 0) && ((uintptr_t)x % 16 == 0);
+        rg->vec_out = (g.Cout % 4 == 0) && ((uintptr_t)c % 16 == 0);
+        rg->T = (rg->inner_out + 15) / 16;
+        return true;
+    }
     rg->vec_in = (rg->inner_in % 4 == 0) && ((uintptr_t)x % 16 == 0);
     rg->vec_out = (g.SP % 4 == 0) && ((uintptr_t)c % 16 == 0);
     // largest start shift of a slice's tiles: 0 when a slice is a multiple of 4 positions,
@@ -553,12 +592,18 @@ hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, co
 {
     const size_t lds = 4 * (size_t)g.Cin * rg.inner_in * sizeof(float);
     const int grid = ring_grid(g, rg, wgs_per_cu);
-    if (rg.vec_in)
-        conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true>
-            <<<dim3(grid), dim3(kMfmaBlock), lds, stream>>>(g, rg, x, w, b, c);
-    else
-        conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false>
-            <<<dim3(grid), dim3(kMfmaBlock), lds, stream>>>(g, rg, x, w, b, c);
+    const dim3 gd(grid), bd(kMfmaBlock);
+    if (g.cl) {
+        if (rg.vec_in)
+            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true, true><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+        else
+            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false, true><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+    } else {
+        if (rg.vec_in)
+            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true, false><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+        else
+            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false, false><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+    }
     return hipGetLastError();
 }
 }  // namespace
@@ -573,7 +618,7 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
     if (!conv_valu_forced() && small) {
         // 16-byte output stores need every box to start on a multiple of 4 positions: B * 62
         // is, SP % 4 == 0 keeps planes aligned
-        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64 && g.W == kC8W && (uintptr_t)x % 16 == 0 &&
+        if (!g.cl && g.dims == 2 && g.Cin == 8 && g.Cout == 64 && g.W == kC8W && (uintptr_t)x % 16 == 0 &&
             (uintptr_t)c % 16 == 0 && g.SP % 4 == 0) {
             static int cus = 0;
             if (cus == 0) {
@@ -597,10 +642,14 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
     }
     const dim3 grid((unsigned)((g.SP + kConvBlock - 1) / kConvBlock), (unsigned)g.N,
                     (unsigned)((g.Cout + kKB - 1) / kKB));
-    if (g.dims == 3)
-        conv_k3_kernel<3><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
+    if (g.dims == 3 && g.cl)
+        conv_k3_kernel<3, true><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
+    else if (g.dims == 3)
+        conv_k3_kernel<3, false><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
+    else if (g.cl)
+        conv_k3_kernel<2, true><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
     else
-        conv_k3_kernel<2><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
+        conv_k3_kernel<2, false><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
     return hipGetLastError();
 }
 

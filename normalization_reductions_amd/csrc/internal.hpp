@@ -67,6 +67,7 @@ struct ConvGeom {
     int64_t N, Cin, Cout;
     int64_t D, H, W;           // input extent (D = 1 for 2-D)
     int64_t OD, OH, OW, SP;    // output extent, SP = OD*OH*OW
+    int cl = 0;                // channels last: x [N, D, H, W, Cin], output [N, SP, Cout]
 };
 
 // Geometry of the persistent conv producer: the output as N * OO outer slices (rows in 2-D,
@@ -106,6 +107,23 @@ struct ChainArgs {
 };
 
 hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Channels-last chain: c [N, SP, C] (C contiguous). A group is (n, k) (instance) or k (batch);
+// its values are C apart. Partials per (n, chunk of positions, k), merged in fixed order.
+// ---------------------------------------------------------------------------------------------
+struct ClGeom {
+    int64_t N, C, SP;
+    int64_t chunk;    // positions per partial
+    int64_t chunks;   // partials per batch item: ceil(SP / chunk)
+    bool batch;
+};
+ClGeom cl_geometry(int64_t N, int64_t C, int64_t SP, bool batch);
+size_t cl_partials_bytes(const ClGeom& g);  // float4 per (n, chunk, k)
+hipError_t launch_cl_stats(const ClGeom& g, const float* c, const float* pre_mul, float4* partials,
+                           float eps, GroupStat* stats, RunningStats run, hipStream_t stream);
+// ChainArgs as for the planar chain, with c and (without the max) out in [N, SP, C] layout.
+hipError_t launch_cl_apply(const ChainArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // Utilities.

@@ -161,6 +161,7 @@ def _desc(**over):
     (dict(in_h=2), 1), (dict(spatial_dims=3, in_d=2), 1), (dict(norm=0), 1), (dict(eps=-1.0), 1),
     (dict(clamp=1, clamp_lo=1.0, clamp_hi=-1.0), 1), (dict(clamp=2), 1), (dict(reduce_max_c=3), 1),
     (dict(pre_mul=FAKE + 2), 2), (dict(N=70000), 3),
+    (dict(channels_last=2), 1), (dict(channels_last=1, C_out=300), 3),
 ])
 def test_conv_rejects(lib, over, status):
     d = _desc(**over)

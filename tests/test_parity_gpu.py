@@ -524,6 +524,93 @@ def test_conv_bn_eval(dev, nra, orc, shape, cout):
                                                      beta=t(bt), out_scale=2.0))
 
 
+# channels last: x [N, spatial, C_in], out [N, spatial, C_out] (or the channel max); the oracle
+# runs on the planar transpose of the same values
+CL_CASES = [
+    # (planar x shape, Cout, batch, reduce_max_c, every optional parameter)
+    ((128, 3, 16, 32, 32), 16, False, True, True),   # the IN3d model's shape, full size
+    ((128, 8, 64, 64), 64, True, False, True),       # the batch-norm model's shape, full size
+    ((2, 3, 9, 11), 5, True, False, True),           # vector-ALU producer
+    ((4, 2, 6, 7, 9), 17, False, True, False),
+    ((3, 1, 5, 6, 7), 20, False, True, True),
+    ((2, 8, 15, 13), 64, False, False, True),        # 2-D matrix-core ring, ragged rows
+    ((1, 8, 3, 64), 64, True, False, True),
+    ((2, 3, 6, 9, 11), 16, False, True, True),       # 3-D matrix-core ring, scalar staging
+    ((3, 3, 5, 7, 8), 16, True, False, True),
+]
+
+
+def _to_cl(a):
+    return np.ascontiguousarray(np.moveaxis(a, 1, -1))
+
+
+@pytest.mark.parametrize("shape,cout,batch,red,full", CL_CASES)
+def test_conv_chain_channels_last(dev, nra, orc, shape, cout, batch, red, full):
+    g = np.random.Generator(np.random.PCG64(len(shape) * 10000 + cout * 7 + shape[0]))
+    x = g.standard_normal(shape).astype(np.float32)
+    dims = len(shape) - 2
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32) if full else None
+    opt = lambda a: a if full else None
+    pm = opt(g.standard_normal(cout).astype(np.float32))
+    gm = opt(g.uniform(0.5, 1.5, cout).astype(np.float32))
+    bt = opt(g.uniform(-0.5, 0.5, cout).astype(np.float32))
+    qm = opt(g.standard_normal(cout).astype(np.float32))
+    clamp = (-0.8, 1.1) if full else None
+    t = lambda a: None if a is None else T(a, dev)
+    out = nra.conv_norm_epilogue_forward(
+        t(_to_cl(x)), t(w), t(b), norm=nra.NR_NORM_BATCH_TRAIN if batch else nra.NR_NORM_INSTANCE,
+        pre_mul=t(pm), gamma=t(gm), beta=t(bt), out_scale=1.5 if full else 1.0, clamp=clamp,
+        post_mul=t(qm), reduce_max_c=red, channels_last=True)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=batch, pre_mul=pm, gamma=gm, beta=bt,
+                                 out_scale=1.5 if full else 1.0, clamp=clamp, post_mul=qm,
+                                 reduce_max_c=red)
+    got = H(out) if red else np.moveaxis(H(out), -1, 1)
+    err = maxerr(got, ref)
+    _log("channels-last chain %s Cout %d batch %s max_c %s: max_abs_err %.3e"
+         % (shape, cout, batch, red, err))
+    assert err <= TOL
+
+
+def test_conv_chain_channels_last_running_statistics(dev, nra, orc):
+    g = np.random.Generator(np.random.PCG64(4242))
+    x = g.standard_normal((4, 3, 6, 10, 12)).astype(np.float32)
+    w = (g.standard_normal((16, 3, 3, 3, 3)) * 0.3).astype(np.float32)
+    b = g.standard_normal(16).astype(np.float32)
+    rm0 = g.uniform(-1, 1, 16).astype(np.float32)
+    rv0 = g.uniform(0.5, 2, 16).astype(np.float32)
+    t = lambda a: T(a, dev)
+    rm, rv = t(rm0), t(rv0)
+    out = nra.conv_norm_epilogue_forward(t(_to_cl(x)), t(w), t(b), norm=nra.NR_NORM_BATCH_TRAIN,
+                                         running_mean=rm, running_var=rv, momentum=0.2,
+                                         channels_last=True)
+    c = orc.conv_k3(x, w, b)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    rm_ref, rv_ref = orc.bn_running_update(mean, var, c.size // 16, rm0, rv0, momentum=0.2)
+    _check_running(rm, rv, rm_ref, rv_ref, "channels-last chain running statistics")
+    ref = orc.conv_norm_epilogue(x, w, b, batch=True)
+    assert maxerr(np.moveaxis(H(out), -1, 1), ref) <= TOL
+
+
+@pytest.mark.parametrize("shape,cout", [((128, 8, 64, 64), 64), ((128, 3, 16, 32, 32), 16),
+                                        ((2, 3, 9, 11), 5), ((1, 8, 15, 13), 64)])
+def test_conv_bn_eval_channels_last(dev, nra, orc, shape, cout):
+    g = np.random.Generator(np.random.PCG64(cout * 31 + len(shape)))
+    x = g.standard_normal(shape).astype(np.float32)
+    dims = len(shape) - 2
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32)
+    rm = g.uniform(-1, 1, cout).astype(np.float32)
+    rv = g.uniform(0.3, 3, cout).astype(np.float32)
+    t = lambda a: T(a, dev)
+    out = nra.conv_bn_eval_forward(t(_to_cl(x)), t(w), t(b), t(rm), t(rv), out_scale=2.0,
+                                   channels_last=True)
+    ref = orc.conv_bn_eval(x, w, b, rm, rv, scale=2.0)
+    err = maxerr(np.moveaxis(H(out), -1, 1), ref)
+    _log("channels-last conv_bn_eval %s Cout %d: max_abs_err %.3e" % (shape, cout, err))
+    assert err <= TOL
+
+
 def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
     # the vector-ALU conv producer (used for shapes without a matrix-core instantiation),
     # forced on the IN3d workload
