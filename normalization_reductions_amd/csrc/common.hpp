@@ -99,10 +99,10 @@ __device__ __forceinline__ unsigned long long xchg_load(unsigned long long* p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Upper bound on polling rounds in a co-residency wait. A round is a short sleep plus two
-// device-coherent loads, so 2^22 rounds is far beyond any legitimate wait (every waiter's
-// siblings are co-resident by construction); it keeps a broken launch from spinning forever:
-// the wait gives up and raises a sticky flag.
+// Upper bound on polling rounds in an exchange wait. A round is a short sleep plus two
+// device-coherent loads, so 2^22 rounds is far beyond any legitimate wait (the siblings a
+// waiter needs are held by running workgroups whenever 16 or more of the grid run); it keeps a
+// starved or broken launch from spinning forever: the wait gives up and raises a sticky flag.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kFlagSpinTimeout = 1u;
 

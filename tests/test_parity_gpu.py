@@ -231,6 +231,21 @@ def test_inorm_workspace_carries_no_state(dev, nra, orc):
         assert nra.workspace_check(ws) == 0
 
 
+def test_cooperative_launch_option(dev, nra, orc, monkeypatch):
+    # the persistent kernels run from a regular launch; NORMRED_COOPERATIVE=1 selects a
+    # cooperative launch of the same grid, which must give bitwise the same result
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(77))
+    x = (g.standard_normal((3, 5, 100000)) * 2 + 1).astype(np.float32)
+    xt = T(x, dev)
+    y_reg = nra.inorm_forward(xt)
+    monkeypatch.setenv("NORMRED_COOPERATIVE", "1")
+    y_coop = nra.inorm_forward(xt)
+    assert torch.equal(y_reg, y_coop)
+    assert maxerr(H(y_coop), orc.instance_norm(x)) <= TOL
+
+
 def test_inorm_empty_batch(dev, nra):
     import torch
 
