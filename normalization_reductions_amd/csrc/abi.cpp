@@ -95,10 +95,11 @@ bool resident_override(int* block, int* vec)
 }
 
 // Pick a read-once configuration and part count for groups of L values of the given kind.
-// Without an override: groups that fit one workgroup (<= 64K values) take the smallest
-// single-workgroup configuration of the kind that holds them (measured faster than splitting
-// such groups); larger groups take the pipelined kernel with 64 KiB parts (256 threads x 16
-// float4), or 128 KiB parts past 32 of those.
+// Without an override: groups that fit a workgroup of up to 512 threads (<= 32K values) take
+// the smallest single-workgroup configuration of the kind that holds them (measured faster
+// than splitting such groups); larger groups take the pipelined kernel with 64 KiB parts (256
+// threads x 16 float4), or 128 KiB parts past 32 of those. (For 64K-value slices, 4 pipelined
+// parts measured 6 % faster than one 1024-thread workgroup per slice.)
 // Grouped kinds (batch norm) need L < 2^21 for their index arithmetic.
 bool choose_resident(int64_t L, bool grouped, bool chain, int* cfg_idx, int* P)
 {
@@ -112,7 +113,7 @@ bool choose_resident(int64_t L, bool grouped, bool chain, int* cfg_idx, int* P)
         if (over && (c.block != ob || c.vec != ov)) continue;
         const int64_t p = (L + c.part_len - 1) / c.part_len;
         if (!c.pipelined) {
-            if (p != 1) continue;
+            if (p != 1 || (!over && c.block > 512)) continue;
         } else {
             if (p < 2 || p > kMaxParts) continue;
             if (!over && c.vec != 16) continue;

@@ -246,6 +246,29 @@ def test_cooperative_launch_option(dev, nra, orc, monkeypatch):
     assert maxerr(H(y_coop), orc.instance_norm(x)) <= TOL
 
 
+def test_inorm_two_streams_concurrently(dev, nra, orc):
+    # two persistent read-once launches in flight on different streams, each with its own
+    # workspace: both must finish with correct results and clean workspace flags
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(91))
+    xs = [(g.standard_normal((4, 64, 131072)) * s + o).astype(np.float32) for s, o in ((1, 0), (3, -2))]
+    xt = [T(x, dev) for x in xs]
+    ys = [torch.empty_like(x) for x in xt]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    wss = [torch.zeros(nra.inorm_workspace_size(4, 64, 131072), dtype=torch.uint8, device=dev)
+           for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                nra.inorm_forward(xt[i], ys[i], workspace=wss[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert nra.workspace_check(wss[i]) == 0
+        assert maxerr(H(ys[i]), orc.instance_norm(xs[i])) <= TOL
+
+
 def test_inorm_empty_batch(dev, nra):
     import torch
 
