@@ -269,6 +269,69 @@ def test_inorm_two_streams_concurrently(dev, nra, orc):
         assert maxerr(H(ys[i]), orc.instance_norm(xs[i])) <= TOL
 
 
+# ------------------------------------------------------------------------------------------
+# Beyond 2^31 elements (64-bit offsets everywhere): ~8.6 GB inputs, sampled parity
+# ------------------------------------------------------------------------------------------
+def _big_normal(shape, seed, dev):
+    import torch
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    return torch.randn(*shape, device=dev, generator=gen)
+
+
+@pytest.mark.parametrize("variant", [0, 2])
+def test_inorm_beyond_2pow31_elements(dev, nra, orc, variant):
+    import torch
+
+    N, C, S = 2, 4100, 262144  # 2,149,580,800 elements: read-once (auto) and split variants
+    x = _big_normal((N, C, S), 0x5EED0101, dev)
+    ws = torch.zeros(nra.inorm_workspace_size(N, C, S), dtype=torch.uint8, device=dev)
+    y = nra.inorm_forward(x, eps=1e-5, workspace=ws, variant=variant)
+    assert nra.workspace_check(ws) == 0
+    pick = _sample_slices(N * C, 5, 17 + variant)
+    xs = x.view(N * C, S)[pick].cpu().numpy()
+    ys = y.view(N * C, S)[pick].cpu().numpy()
+    err = maxerr(ys, orc.instance_norm_slices(xs))
+    _log("inorm beyond 2^31 elements, variant %d: max_abs_err %.3e over %d slices" % (variant, err, len(pick)))
+    del x, y, ws
+    torch.cuda.empty_cache()
+    assert err <= TOL
+
+
+def test_inorm_huge_slices_split_path(dev, nra, orc):
+    import torch
+
+    N, C, S = 1, 130, (1 << 24) + 4  # 16.8M values per slice: beyond any read-once part count
+    x = _big_normal((N, C, S), 0x5EED0102, dev)
+    x.mul_(3.0).add_(-7.0)
+    y = nra.inorm_forward(x)
+    pick = [0, 64, 129]
+    xs = x.view(C, S)[pick].cpu().numpy()
+    ys = y.view(C, S)[pick].cpu().numpy()
+    err = maxerr(ys, orc.instance_norm_slices(xs))
+    _log("inorm 130 slices of 2^24+4: max_abs_err %.3e" % err)
+    del x, y
+    torch.cuda.empty_cache()
+    assert err <= TOL
+
+
+def test_bn_train_beyond_2pow31_elements(dev, nra, orc):
+    import torch
+
+    N, C, S = 128, 64, 262148  # 2.15e9 elements; 33.6M values per channel (split path)
+    x = _big_normal((N, C, S), 0x5EED0103, dev)
+    y = nra.bn_train_forward(x, out_scale=2.0)
+    chans = [0, 63]
+    xs = x[:, chans].cpu().numpy()
+    ys = y[:, chans].cpu().numpy()
+    err = maxerr(ys, orc.batch_norm_train(xs, scale=2.0))
+    _log("bn_train beyond 2^31 elements: max_abs_err %.3e on channels %s" % (err, chans))
+    del x, y
+    torch.cuda.empty_cache()
+    assert err <= TOL
+
+
 def test_inorm_empty_batch(dev, nra):
     import torch
 
