@@ -570,17 +570,19 @@ bool make_ring(const ConvGeom& g, const float* x, const float* c, int PF, ConvRi
     return true;
 }
 
+// Compute units of the current device (the runtime caches device attributes).
+int device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return 256;
+    return cus;
+}
+
 int ring_grid(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            cus = 256;
-        else
-            cus = prop.multiProcessorCount;
-    }
+    const int cus = device_cus();
     if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs_per_cu = std::max(1, atoi(e));
     const int64_t total = g.N * (int64_t)rg.OO * rg.T;
     return (int)std::max<int64_t>(1, std::min<int64_t>(total, (int64_t)cus * wgs_per_cu));
@@ -620,13 +622,7 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
         // is, SP % 4 == 0 keeps planes aligned
         if (!g.cl && g.dims == 2 && g.Cin == 8 && g.Cout == 64 && g.W == kC8W && (uintptr_t)x % 16 == 0 &&
             (uintptr_t)c % 16 == 0 && g.SP % 4 == 0) {
-            static int cus = 0;
-            if (cus == 0) {
-                int dev = 0;
-                hipDeviceProp_t prop;
-                cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-                          ? prop.multiProcessorCount : 256;
-            }
+            const int cus = device_cus();
             int wgs = 2;  // per CU: one wave per SIMD each, the most its VGPR use allows
             if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs = std::max(1, atoi(e));
             constexpr int B = 4;  // output rows per box (2 rows measured ~8 % slower)
