@@ -228,8 +228,8 @@ nr_status conv_bn_eval_forward(const nr_conv_norm_desc* d, const float* x, const
 nr_status nr_workspace_clear(void* workspace, size_t bytes, hipStream_t stream);
 
 /* Reads the workspace's sticky error word (synchronizes `stream` first). *flags_out = 0 when
- * every co-resident exchange completed; bit 0 = a bounded wait gave up (results of that call
- * are invalid). Clears the word afterwards. */
+ * every exchange wait completed; bit 0 = a bounded wait gave up (results of that call are
+ * invalid). Clears the word afterwards. */
 nr_status nr_workspace_check(void* workspace, size_t bytes, hipStream_t stream, uint32_t* flags_out);
 
 /* Plain streaming copy dst[i] = src[i], i < n, with 16-byte loads/stores: the HBM ceiling the

@@ -2,7 +2,9 @@
 
 Bar: max |gpu - oracle| <= 1e-4 over every compared output element (fp32 outputs), the
 tolerance the workloads state; bit-identical results across repeated runs; the workspace's
-error flags stay clear. All inputs come from the seeded generators in synth/.
+error flags stay clear. Inputs are seeded and synthetic: synth/'s generators, torch's seeded
+device generator for the tensors beyond 2^31 elements, and the native client's counter-based
+generator (SplitMix64).
 """
 import os
 
@@ -439,6 +441,19 @@ def test_bn_train(dev, nra, orc, shape):
     assert torch.equal(xt, y)
 
 
+@pytest.mark.parametrize("shape", [(8, 4, 4096), (16, 2, 65536), (4, 3, 1001)])
+def test_bn_train_large_offset_small_spread(dev, nra, orc, shape):
+    # mean ~1000, spread ~0.01: the statistics must not lose the spread to the offset
+    # (single-workgroup, pipelined and split paths)
+    N, C, S = shape
+    g = np.random.Generator(np.random.PCG64(N * 31 + S))
+    x = (1000.0 + 0.01 * g.standard_normal(shape) + g.uniform(-1, 1, (1, C, 1))).astype(np.float32)
+    y = nra.bn_train_forward(T(x, dev))
+    err = maxerr(H(y), orc.batch_norm_train(x))
+    _log("bn_train offset 1000, spread 0.01 %s: max_abs_err %.3e" % (shape, err))
+    assert err <= TOL
+
+
 # running statistics: resident single-workgroup, pipelined, split (S % 4 != 0) and the
 # beyond-index-range split path; two steps in a row so the update compounds
 BN_RUNNING_SHAPES = [(128, 64, 3844), (5, 2, 7), (2, 4, 4100), (33, 2, 16000), (65, 2, 32768)]
@@ -726,6 +741,24 @@ def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
                                  pre_mul=inp["mult"], clamp=inp["clamp"], post_mul=inp["mult"],
                                  reduce_max_c=True)
     assert maxerr(H(out), ref) <= TOL
+
+
+def test_native_c_abi_roundtrip(dev, orc, tmp_path):
+    # a plain C++ program (tests/native/abi_roundtrip.cpp, built by build()) drives the C ABI
+    # with hipMalloc'd buffers and its own stream; its outputs must match the oracle
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "abi_roundtrip")
+    assert os.path.exists(exe), "build the native client first (__graft_entry__.build())"
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    _log("native client: rc %d, stdout %r, stderr %r" % (r.returncode, r.stdout[-200:], r.stderr[-400:]))
+    assert r.returncode == 0
+    shape = (3, 5, 100004)
+    x = np.fromfile(tmp_path / "x.bin", np.float32).reshape(shape)
+    y = np.fromfile(tmp_path / "inorm.bin", np.float32).reshape(shape)
+    z = np.fromfile(tmp_path / "bn.bin", np.float32).reshape(shape)
+    assert maxerr(y, orc.instance_norm(x)) <= TOL
+    assert maxerr(z, orc.batch_norm_train(x, scale=2.0)) <= TOL
 
 
 def test_stream_copy(dev, nra):
