@@ -175,6 +175,58 @@ __global__ __launch_bounds__(kClBlock) void cl_apply_kernel(ChainArgs a)
     if (a.reduce_max_c) a.out[n * a.SP + i] = mx;
 }
 
+// C / 4 = TPP lanes per position (C a multiple of 4, TPP a power of two <= 64): lane j of a
+// position handles channels 4j..4j+3 with one 16-byte load, so each load instruction of a wave
+// reads 1 KiB contiguously; the max over channels then finishes with log2(TPP) shuffles
+// (lower lanes first). Coefficients staged in LDS as in cl_apply_kernel.
+__global__ __launch_bounds__(kClBlock) void cl_apply_lanes_kernel(ChainArgs a, int tpp)
+{
+    extern __shared__ float coef_raw[];  // [C] ClCoef
+    ClCoef* coef = reinterpret_cast<ClCoef*>(coef_raw);
+    const int64_t n = blockIdx.y;
+    const int C = (int)a.Cout;
+    for (int k = threadIdx.x; k < C; k += kClBlock) {
+        const GroupStat s = a.stats[a.batch ? k : n * a.Cout + k];
+        ClCoef q;
+        q.pm = a.pre_mul ? a.pre_mul[k] : 1.f;
+        q.pivot = s.pivot;
+        q.mean_d = s.mean_d;
+        q.A = s.rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale;
+        q.B = (a.beta ? a.beta[k] : 0.f) * a.out_scale;
+        q.post = a.post_mul ? a.post_mul[k] : 1.f;
+        coef[k] = q;
+    }
+    __syncthreads();
+    const int per_block = kClBlock / tpp;
+    const int j = threadIdx.x % tpp;
+    const int64_t i = (int64_t)blockIdx.x * per_block + threadIdx.x / tpp;  // position
+    const bool live = i < a.SP;
+    f4 z = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (live) {
+        const f4 v = *reinterpret_cast<const f4*>(a.c + (n * a.SP + i) * a.Cout + 4 * j);
+        auto one = [&](int k, float x) {
+            const ClCoef q = coef[k];
+            float r = (fmaf(x, q.pm, -q.pivot) - q.mean_d) * q.A + q.B;
+            if (a.clamp) r = fminf(fmaxf(r, a.lo), a.hi);
+            return r * q.post;
+        };
+        z.x = one(4 * j, v.x);
+        z.y = one(4 * j + 1, v.y);
+        z.z = one(4 * j + 2, v.z);
+        z.w = one(4 * j + 3, v.w);
+        if (!a.reduce_max_c) *reinterpret_cast<f4*>(a.out + (n * a.SP + i) * a.Cout + 4 * j) = z;
+    }
+    if (a.reduce_max_c) {
+        float m = fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w));
+        const int lane = threadIdx.x & (kWave - 1);
+        for (int off = 1; off < tpp; off <<= 1) {  // tpp divides 64: positions never straddle waves
+            const float o = __shfl_xor(m, off);
+            m = (lane & off) ? fmaxf(o, m) : fmaxf(m, o);
+        }
+        if (live && j == 0) a.out[n * a.SP + i] = m;
+    }
+}
+
 }  // namespace
 
 ClGeom cl_geometry(int64_t N, int64_t C, int64_t SP, bool batch)
@@ -212,6 +264,13 @@ hipError_t launch_cl_apply(const ChainArgs& a, hipStream_t stream)
     const size_t lds = (size_t)a.Cout * sizeof(ClCoef);
     const bool vec = a.Cout % 4 == 0 && (uintptr_t)a.c % 16 == 0 &&
                      (a.reduce_max_c || (uintptr_t)a.out % 16 == 0);
+    const int64_t tpp = a.Cout / 4;
+    if (vec && tpp <= kWave && (tpp & (tpp - 1)) == 0) {
+        const int64_t per_block = kClBlock / tpp;
+        const dim3 g2((unsigned)((a.SP + per_block - 1) / per_block), (unsigned)a.N);
+        cl_apply_lanes_kernel<<<g2, dim3(kClBlock), lds, stream>>>(a, (int)tpp);
+        return hipGetLastError();
+    }
     if (vec)
         cl_apply_kernel<true><<<grid, dim3(kClBlock), lds, stream>>>(a);
     else
