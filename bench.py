@@ -244,6 +244,31 @@ def extras(torch, nra, x, y, steps, warmup):
         "ms": round(per, 4), "conv_TFLOPs_over_chain_time": round(2 * 128 * 16 * 12600 * 81 / (per / 1e3) / 1e12, 2)}
     log("conv3d+IN3d+clamp+max_c: %.4f ms" % per)
 
+    # both chains captured once in a HIP graph (their workspaces allocated beforehand) and
+    # replayed: the same kernels without per-call host launch overhead
+    gs = torch.cuda.Stream(device=dev)
+    w4 = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)  # holds either chain's plan
+    w5 = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
+    g4f = lambda: nra.conv_norm_epilogue_forward(*a4, out=o4, norm=nra.NR_NORM_BATCH_TRAIN,
+                                                 gamma=g4, beta=be4, out_scale=2.0,
+                                                 workspace=w4, stream=gs)
+    g5f = lambda: nra.conv_norm_epilogue_forward(*a5, out=o5, norm=nra.NR_NORM_INSTANCE,
+                                                 pre_mul=m5, clamp=(-1.0, 1.0), post_mul=m5,
+                                                 reduce_max_c=True, workspace=w5, stream=gs)
+    for name, fn in (("conv2d_bn_train_x2_graph_replay", g4f), ("conv3d_in3d_clamp_maxc_graph_replay", g5f)):
+        gs.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(gs):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            fn()
+        torch.cuda.synchronize()
+        tot, per, med = time_calls(graph.replay, steps, warmup, torch, flush)
+        out[name] = {"ms": round(per, 4)}
+        log("%s: %.4f ms" % (name, per))
+        del graph
+
     # the same IN3d chain with channels-last input and conv output
     x5cl = a5[0].permute(0, 2, 3, 4, 1).contiguous()
     f5cl = lambda: nra.conv_norm_epilogue_forward(x5cl, a5[1], a5[2], out=o5,

@@ -743,6 +743,58 @@ def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
     assert maxerr(H(out), ref) <= TOL
 
 
+def test_graph_capture_and_replay(dev, nra, orc):
+    # every launch of these entry points can be captured: no hipMemsetAsync (fill kernels
+    # instead), no synchronization, regular launches. Capture instance norm (read-once
+    # pipelined), batch norm and the IN3d conv chain once, then replay three times with eager
+    # changes of the inputs in between, checking every replay against the oracle.
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(5150))
+    xi = T(g.standard_normal((2, 8, 100000)).astype(np.float32), dev)
+    xb = T(g.standard_normal((16, 8, 3000)).astype(np.float32), dev)
+    i5 = synth.host_inputs(5)
+    xc = T(np.ascontiguousarray(i5["x"][:4]), dev)
+    wc, bc, mc = T(i5["w"], dev), T(i5["b"], dev), T(i5["mult"], dev)
+    yi, yb = torch.empty_like(xi), torch.empty_like(xb)
+    yc = torch.empty((4, 14, 30, 30), device=dev)
+    s = torch.cuda.Stream(device=dev)
+    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(3)]
+    chain = dict(norm=nra.NR_NORM_INSTANCE, pre_mul=mc, clamp=(-1.0, 1.0), post_mul=mc,
+                 reduce_max_c=True)
+
+    def work():
+        nra.inorm_forward(xi, yi, workspace=ws[0], stream=s)
+        nra.bn_train_forward(xb, yb, out_scale=2.0, workspace=ws[1], stream=s)
+        nra.conv_norm_epilogue_forward(xc, wc, bc, yc, workspace=ws[2], stream=s, **chain)
+
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        work()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.no_grad():
+            xi.mul_(1.5).add_(0.25)
+            xb.mul_(0.5).sub_(1.0)
+            xc.mul_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for w in ws:
+            assert nra.workspace_check(w) == 0
+        e1 = maxerr(H(yi), orc.instance_norm(H(xi)))
+        e2 = maxerr(H(yb), orc.batch_norm_train(H(xb), scale=2.0))
+        e3 = maxerr(H(yc), orc.conv_norm_epilogue(H(xc), i5["w"], i5["b"], batch=False,
+                                                  pre_mul=i5["mult"], clamp=(-1.0, 1.0),
+                                                  post_mul=i5["mult"], reduce_max_c=True))
+        _log("graph replay %d: max_abs_err %.3e %.3e %.3e" % (rep, e1, e2, e3))
+        assert max(e1, e2, e3) <= TOL
+
+
 def test_native_c_abi_roundtrip(dev, orc, tmp_path):
     # a plain C++ program (tests/native/abi_roundtrip.cpp, built by build()) drives the C ABI
     # with hipMalloc'd buffers and its own stream; its outputs must match the oracle
