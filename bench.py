@@ -335,7 +335,7 @@ def main() -> int:
     launch_min = time_calls.last[0]
     flags = nra.workspace_check(ws)
     if flags:
-        log("workspace flags %#x: a co-resident wait gave up; results invalid" % flags)
+        log("workspace flags %#x: an exchange wait gave up; results invalid" % flags)
         return 1
     ms = total_ms / args.steps
     value = MIN_BYTES / (ms / 1e3) / 1e9

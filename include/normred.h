@@ -82,8 +82,8 @@ nr_status inorm_forward(const float* x, float* y, int64_t N, int64_t C, int64_t 
 
 /* Kernel variants for inorm_forward_ex (benchmarks and tests; inorm_forward = AUTO). */
 #define NR_VARIANT_AUTO 0     /* the library's choice for the shape */
-#define NR_VARIANT_RESIDENT 1 /* read-once: each slice held in registers, split over 1..16
-                                 co-resident workgroups that exchange partial statistics */
+#define NR_VARIANT_RESIDENT 1 /* read-once: each slice held in registers, split over 1..32
+                                 concurrent workgroups that exchange partial statistics */
 #define NR_VARIANT_SPLIT 2    /* streaming two-pass: partial statistics per chunk, a fixed-order
                                  merge, then a normalize pass (reads x twice) */
 

@@ -83,7 +83,7 @@ __device__ __forceinline__ void st_stream(f4* p, f4 v) { __builtin_nontemporal_s
 __device__ __forceinline__ float ld_stream1(const float* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream1(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
-// Exchange words between co-resident workgroups: 64-bit, a tag in the high half and an fp32
+// Exchange words between the workgroups of a group's parts: 64-bit, a tag in the high half and an fp32
 // payload in the low half. They are only ever accessed with relaxed agent-scope atomics, so
 // each word is read whole and coherently across the XCDs' L2s; a reader accepts a word only
 // when its tag says it was written by the current launch.

@@ -8,10 +8,10 @@
 
 namespace nr {
 
-constexpr int kMaxParts = 32;  // parts per statistics group in the co-resident kernels
+constexpr int kMaxParts = 32;  // parts per statistics group in the read-once kernels
 
 // Read-once ("resident") normalization: each statistics group (one slice for instance norm, the
-// N slices of a channel for batch norm) split over P co-resident workgroups, each holding its
+// N slices of a channel for batch norm) split over P workgroups that run concurrently, each holding its
 // part in registers.
 struct ResidentCfg {
     int block;       // threads per workgroup
@@ -64,7 +64,8 @@ inline size_t resident_ws_bytes(int64_t groups, int P)
     return P > 1 ? kCounterBytes + (size_t)groups * (size_t)P * 2 * sizeof(unsigned long long) : 0;
 }
 
-// Largest grid the kernel can have fully co-resident (0 if the configuration is unknown).
+// Persistent grid of the pipelined kernel: CUs x min(occupancy, workgroups per CU wanted)
+// (0 if the configuration is unknown).
 int resident_max_grid(const ResidentCfg& cfg);
 hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStream_t stream);
 

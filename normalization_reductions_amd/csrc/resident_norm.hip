@@ -533,7 +533,7 @@ hipError_t launch_resident(const ResidentCfg& cfg, const ResidentArgs& a, hipStr
     const int64_t units = a.groups * a.P;
     int64_t grid = resident_max_grid(cfg);
     if (grid > units) grid = units;
-    if (grid < a.P) return hipErrorCooperativeLaunchTooLarge;  // a grid that can hold a group
+    if (grid < a.P) return hipErrorInvalidConfiguration;  // the grid must cover a whole group
     // counter + slots start zeroed for every launch (they carry nothing between calls)
     const hipError_t e = launch_fill_zero(a.counter, resident_ws_bytes(a.groups, a.P), stream);
     if (e != hipSuccess) return e;
