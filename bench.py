@@ -67,23 +67,29 @@ HEADLINE_KERNEL = "norm_pipelined_kernel<256, 16, false, false>"
 COPY_KERNEL = "copy_vec_kernel"
 
 
-def _counter_rows(path, counter, needle):
+def _counter_rows(path, counter, needle, before=None):
+    """Counter values of the dispatches of kernel `needle`, in dispatch order; with `before`,
+    only those dispatched before the first dispatch of kernel `before`."""
     import csv
 
     with open(path, newline="") as f:
-        rows = [r for r in csv.DictReader(f)
-                if r["Counter_Name"] == counter and needle in r["Kernel_Name"]]
+        rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-    return [float(r["Counter_Value"]) for r in rows]
+    if before is not None:
+        first = next((int(r["Dispatch_Id"]) for r in rows if before in r["Kernel_Name"]), None)
+        if first is not None:
+            rows = [r for r in rows if int(r["Dispatch_Id"]) < first]
+    return [float(r["Counter_Value"]) for r in rows if needle in r["Kernel_Name"]]
 
 
 def traffic_summary(fetch_csv, write_csv):
     """Host-only: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE;
     csv output) into the per-launch HBM byte count of the headline kernel. Each counter is
     calibrated by what it reads for the plain copy kernel of the same run, which moves exactly
-    MIN_BYTES / 2 each way."""
-    kf = _counter_rows(fetch_csv, "FETCH_SIZE", HEADLINE_KERNEL)
-    kw = _counter_rows(write_csv, "WRITE_SIZE", HEADLINE_KERNEL)
+    MIN_BYTES / 2 each way. Only the headline launches count: those before the copy kernel's
+    first launch (the smaller workloads timed afterwards launch the same kernel)."""
+    kf = _counter_rows(fetch_csv, "FETCH_SIZE", HEADLINE_KERNEL, before=COPY_KERNEL)
+    kw = _counter_rows(write_csv, "WRITE_SIZE", HEADLINE_KERNEL, before=COPY_KERNEL)
     cf = _counter_rows(fetch_csv, "FETCH_SIZE", COPY_KERNEL)
     cw = _counter_rows(write_csv, "WRITE_SIZE", COPY_KERNEL)
     if not (kf and kw and cf and cw):
