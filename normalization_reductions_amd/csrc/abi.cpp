@@ -325,8 +325,9 @@ nr_status check_desc(const nr_conv_norm_desc* d, ConvGeom* g, const char* fn)
 
 struct ChainLayout {
     bool resident = false;  // normalize in place in `out` with a read-once kernel
+    bool recompute = false; // batch norm by recomputing the conv (2-D matrix producer shape)
     int cfg_idx = -1, P = 0;
-    size_t exch = 0;
+    size_t exch = 0, c8part = 0, c8stats = 0;
     size_t cbuf = 0, partials = 0, stats = 0, bytes = 0;
     SplitGeom sg;
     ClGeom cg;              // channels last
@@ -357,6 +358,17 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
         return L;
     }
     const int64_t len = batch ? g.N * g.SP : g.SP;
+    if (batch && !reduce_max_c && conv2d_c8_shape(g)) {
+        // batch norm on the 2-D matrix producer's shape: statistics pass, merge, and the conv
+        // again with the chain epilogue (no conv output in HBM). The read-once plan's exchange
+        // slots follow, for calls whose pointers the producer cannot take.
+        L.recompute = true;
+        const int64_t G = std::min<int64_t>(g.N * ((g.OH + 3) / 4), kC8MaxGrid);
+        L.c8part = off;
+        off = align_up(off + (size_t)(g.Cout * G) * sizeof(float4), kWsAlign);
+        L.c8stats = off;
+        off = align_up(off + (size_t)g.Cout * sizeof(GroupStat), kWsAlign);
+    }
     if (!reduce_max_c && g.SP % 4 == 0 && choose_resident(len, batch, true, &L.cfg_idx, &L.P) &&
         groups * L.P <= 0xF0000000LL && groups <= 0x7fffffffLL) {
         L.resident = true;
@@ -575,6 +587,23 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         a.post_mul = d->post_mul;
         a.reduce_max_c = d->reduce_max_c;
         e = launch_cl_apply(a, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
+    if (L.recompute && conv2d_c8_recompute(g, x, out)) {
+        C8Chain c8;
+        c8.pre_mul = d->pre_mul;
+        c8.part = ws_at<float4>(workspace, L.c8part);
+        c8.gamma = d->gamma;
+        c8.beta = d->beta;
+        c8.out_scale = d->out_scale;
+        c8.clamp = d->clamp;
+        c8.lo = d->clamp_lo;
+        c8.hi = d->clamp_hi;
+        c8.post_mul = d->post_mul;
+        const hipError_t e = launch_conv2d_c8_bn_chain(
+            g, x, w, b, out, c8, ws_at<GroupStat>(workspace, L.c8stats), d->eps,
+            RunningStats{d->running_mean, d->running_var, d->momentum}, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }

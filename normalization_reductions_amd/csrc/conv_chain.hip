@@ -344,11 +344,17 @@ __global__ __launch_bounds__(256) void conv2d_c8_mfma32_kernel(ConvGeom g,
     const int64_t HW = g.H * W;
     const int nbox = (OH + B - 1) / B;
 
+    // B operands: the workgroup reads W once with coalesced loads into LDS (the window buffers
+    // are free until the first window is staged); each lane then takes its 72 values from there
+    static_assert(kC8Cout * kC8K <= 2 * WIN, "W fits the window buffers");
+    for (int i = (int)threadIdx.x; i < kC8Cout * kC8K; i += 256) win[i] = w[i];
+    __syncthreads();
     float bw[2][kC8Steps];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int s = 0; s < kC8Steps; ++s) bw[nt][s] = w[(nt * 32 + m) * kC8K + 2 * s + kk];
+        for (int s = 0; s < kC8Steps; ++s) bw[nt][s] = win[(nt * 32 + m) * kC8K + 2 * s + kk];
+    __syncthreads();
     const float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
 
     const int64_t total = g.N * (int64_t)nbox;
@@ -432,6 +438,337 @@ __global__ __launch_bounds__(256) void conv2d_c8_mfma32_kernel(ConvGeom g,
         if (more) drop(buf ^ 1);
         __syncthreads();
         buf ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same 2-D producer with its fp32 products formed on the bf16 matrix pipe. Every fp32
+// value v splits exactly into three bf16 parts, v = h + m + l + e: h = RNE(v), m = RNE(v - h),
+// l = RNE(v - h - m), where both differences are exact in fp32, and |e| <= 2^-24 |v|. A
+// product x*w is taken as hh + hm + mh + mm + hl + lh. The dropped terms (ml, lm, ll) and the
+// two remainders e are each at most 2^-24 |x w|, the size of one fp32 rounding, so the conv
+// keeps fp32 accuracy. One v_mfma_f32_32x32x16_bf16 forms 16384 products in about half the
+// time the fp32 32x32x2 instruction takes for 2048, so the six passes need 2.4x fewer matrix
+// cycles than fp32 (K = 72 padded to 80).
+//
+// K order: a lane-half supplies one 3x3 tap with all 8 input channels, 8 bf16 that one 16-byte
+// LDS read fetches, so the staged window is channels-last: [split][row][column][channel].
+// Chunk q pairs tap 2q (lanes 0..31) with tap 2q + 1 (lanes 32..63); the tenth tap is padding
+// with zero weights whose lanes re-read tap 8, so the operand stays finite. A and B map
+// (lane-half, element) to k the same way, so the products pair up in whatever order the
+// instruction sums them. D has the 32x32 layout of the fp32 kernel above.
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef unsigned int mu4 __attribute__((ext_vector_type(4)));
+typedef unsigned int mu2 __attribute__((ext_vector_type(2)));
+constexpr int kBfChunks = 5;  // K = 72 -> 80: chunks of two taps x 8 channels
+
+__device__ __forceinline__ unsigned bf16_rne(float v)
+{
+    const unsigned u = __float_as_uint(v);  // finite inputs: round to nearest even
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(unsigned h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsigned& l)
+{
+    h = bf16_rne(v);
+    const float r1 = v - bf16_value(h);
+    m = bf16_rne(r1);
+    l = bf16_rne(r1 - bf16_value(m));
+}
+
+// Three modes share the producer: kC8Conv stores the conv output; kC8Stats stores nothing and
+// writes each workgroup's per-channel (count, mean, M2) of the values (conv + bias) * pre_mul,
+// for batch-norm statistics; kC8Apply recomputes the conv and stores the normalized chain
+// output ((v - mean) * rstd * gamma + beta) * out_scale, clamped, times post_mul, in the order
+// the chain epilogue uses.
+enum { kC8Conv = 0, kC8Stats = 1, kC8Apply = 2 };
+
+template <int B, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const float* __restrict__ w,
+                             const float* __restrict__ b, float* __restrict__ c, C8Chain e)
+{
+    constexpr int W = kC8W, OW = W - 2;
+    constexpr int ROWS = B + 2;                    // input rows a box reads
+    constexpr int SPLIT = ROWS * W * kC8Cin;       // bf16 of one split of a staged window
+    constexpr int WIN = 3 * SPLIT;                 // bf16 of one staged window
+    constexpr int ITEMS = ROWS * (W / 4) * 2;      // staging items: row x 4 columns x 4 channels
+    static_assert(ITEMS <= 256, "one staging item per thread");
+    __shared__ __attribute__((aligned(16))) unsigned short win[2 * WIN];
+    const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = l & 31, kk = l >> 5;
+    const int OH = (int)g.OH;
+    const int64_t HW = g.H * W;
+    const int nbox = (OH + B - 1) / B;
+
+    // B operands: lane l holds W[n][0..7][tap 2q + l/32] for n = 32 nt + l%32, in three splits.
+    // The workgroup reads W once with coalesced loads, splits each value, and lays the splits
+    // out in LDS as [nt][q][split][lane] x 8 bf16, from where every lane takes its 30 operands
+    // with 16-byte reads (gathering them per lane touched a cache line per lane and load).
+    // The window buffers hold them until the first window is staged.
+    static_assert(2 * kBfChunks * 3 * 64 * 8 <= 2 * WIN, "operand staging fits the window buffers");
+    static_assert(4 * kC8Cout * sizeof(Stat) <= 2 * WIN * sizeof(unsigned short), "partials fit");
+    for (int i = (int)threadIdx.x; i < 2 * 3 * 32; i += 256) {  // the padding tap's operands
+        const int nt = i / 96, sp = (i / 32) % 3, lane = 32 + i % 32;
+        *reinterpret_cast<mu4*>(win + (((nt * kBfChunks + kBfChunks - 1) * 3 + sp) * 64 + lane) * 8) = mu4{0, 0, 0, 0};
+    }
+    for (int i = (int)threadIdx.x; i < kC8Cout * kC8K; i += 256) {
+        const int n = i / kC8K, rem = i - n * kC8K, ci = rem / 9, tap = rem - ci * 9;
+        unsigned h, mm, lo;
+        split3(w[i], h, mm, lo);
+        unsigned short* d = win + (((n >> 5) * kBfChunks + (tap >> 1)) * 3 * 64 + (n & 31) + 32 * (tap & 1)) * 8 + ci;
+        d[0] = (unsigned short)h;
+        d[64 * 8] = (unsigned short)mm;
+        d[2 * 64 * 8] = (unsigned short)lo;
+    }
+    __syncthreads();
+    bf8 wb[2][kBfChunks][3];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int q = 0; q < kBfChunks; ++q)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp)
+                wb[nt][q][sp] = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(win + (((nt * kBfChunks + q) * 3 + sp) * 64 + l) * 8));
+    __syncthreads();
+    const float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
+    // per-channel factors of this lane's two channels m and 32 + m
+    float pm0 = 1.f, pm1 = 1.f, mu0 = 0.f, mu1 = 0.f, A0 = 1.f, A1 = 1.f, B0 = 0.f, B1 = 0.f, q0 = 1.f, q1 = 1.f;
+    if (MODE != kC8Conv && e.pre_mul) {
+        pm0 = e.pre_mul[m];
+        pm1 = e.pre_mul[32 + m];
+    }
+    if (MODE == kC8Apply) {
+        const GroupStat s0 = e.stats[m], s1 = e.stats[32 + m];
+        mu0 = s0.pivot + s0.mean_d;
+        mu1 = s1.pivot + s1.mean_d;
+        A0 = s0.rstd * (e.gamma ? e.gamma[m] : 1.f) * e.out_scale;
+        A1 = s1.rstd * (e.gamma ? e.gamma[32 + m] : 1.f) * e.out_scale;
+        B0 = (e.beta ? e.beta[m] : 0.f) * e.out_scale;
+        B1 = (e.beta ? e.beta[32 + m] : 0.f) * e.out_scale;
+        if (e.post_mul) {
+            q0 = e.post_mul[m];
+            q1 = e.post_mul[32 + m];
+        }
+    }
+    Stat run0 = stat_empty(), run1 = stat_empty();
+
+    const int64_t total = g.N * (int64_t)nbox;
+    const int64_t begin = total * blockIdx.x / gridDim.x;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    // staging item of this thread: window row, 4 columns, 4 channels (consecutive threads take
+    // consecutive columns, so each channel's loads are coalesced)
+    const int it = threadIdx.x;
+    const int srow = it >> 5, scq = (it >> 4) & 1, sj = it & 15;
+    mf4 pf[4] = {};
+    auto fetch = [&](int64_t box) {
+        const int64_t n = box / nbox;
+        const int o0 = (int)(box - n * nbox) * B;
+        const int rows = min(B, OH - o0) + 2;  // rows past the box's need are not loaded
+        if (it < ITEMS && srow < rows) {
+            const float* xs = x + (n * kC8Cin + 4 * scq) * HW + (int64_t)(o0 + srow) * W + 4 * sj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const mf4*>(xs + i * HW);
+        }
+    };
+    auto drop = [&](int buf) {
+        if (it < ITEMS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                unsigned h[4], mm[4], lo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) split3(pf[i][e], h[i], mm[i], lo[i]);
+                unsigned short* d = win + buf * WIN + (srow * W + 4 * sj + e) * kC8Cin + 4 * scq;
+                *reinterpret_cast<mu2*>(d) = mu2{h[0] | h[1] << 16, h[2] | h[3] << 16};
+                *reinterpret_cast<mu2*>(d + SPLIT) = mu2{mm[0] | mm[1] << 16, mm[2] | mm[3] << 16};
+                *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
+            }
+        }
+    };
+
+    if (begin >= end) {  // (the grid never exceeds the boxes; an empty partial all the same)
+        if (MODE == kC8Stats && threadIdx.x < kC8Cout)
+            e.part[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = float4{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
+    fetch(begin);
+    drop(0);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t box = begin; box < end; ++box) {
+        const bool more = box + 1 < end;
+        if (more) fetch(box + 1);
+
+        const int64_t n = box / nbox;
+        const int o0 = (int)(box - n * nbox) * B;
+        const int BP = min(B, OH - o0) * OW;  // positions in this box: a multiple of 4, >= 62
+        float* c0 = c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
+        float* c1 = c0 + 32 * g.SP;
+        // exactly two tiles per wave, each 32 whole positions of the box: the last tile ends at
+        // the box's last position (overlapping the one before), and waves with no tile left
+        // repeat the last. Overlaps rewrite bitwise-identical values, and every lane issues the
+        // same 16 stores per box, so the wait for the next box's loads need not wait for them.
+        const int tiles = (BP + 31) / 32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ts = min(32 * min(wave + 4 * i, tiles - 1), BP - 32);
+            const int p = ts + m;
+            const int r = p / OW;
+            // window position of this lane's tap (0, 0), then the lane-half distances: one
+            // column (chunks 0, 2, 3: taps 0|1, 4|5, 6|7), W - 2 (chunk 1: taps 2|3), none
+            // (chunk 4: tap 8 | padding)
+            const unsigned short* a0 = win + buf * WIN + (r * W + (p - r * OW)) * kC8Cin;
+            const unsigned short* a1 = a0 + kk * kC8Cin;
+            const unsigned short* a2 = a0 + kk * (W - 2) * kC8Cin;
+            mf16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int q = 0; q < kBfChunks; ++q) {
+                const int off = (q == 0 ? 0 : q == 1 ? 2 : q == 2 ? W + 1 : q == 3 ? 2 * W : 2 * W + 2) * kC8Cin;
+                const unsigned short* a = q == 1 ? a2 : q == 4 ? a0 : a1;
+                const bf8 ah = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off));
+                const bf8 am = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + SPLIT));
+                const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + 2 * SPLIT));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][1], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][2], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][2], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[0][q][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[1][q][0], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][1], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][0], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][0], acc1, 0, 0, 0);
+            }
+            if (MODE == kC8Stats) {
+                // positions this tile owns: from 32 t on for a tile t < tiles (an overlapping
+                // last tile starts earlier), none for a repeated tile
+                const int t = wave + 4 * i;
+                const int own = t < tiles ? 32 * t : BP;
+                float v0[16], v1[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    v0[r] = (acc0[r] + bias0) * pm0;
+                    v1[r] = (acc1[r] + bias1) * pm1;
+                }
+                if (ts == own) {  // the whole tile is owned (all but a box's last or repeated tiles)
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        s0 += v0[r];
+                        s1 += v1[r];
+                    }
+                    const float mean0 = s0 * 0.0625f, mean1 = s1 * 0.0625f;
+                    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        d0 = fmaf(v0[r] - mean0, v0[r] - mean0, d0);
+                        d1 = fmaf(v1[r] - mean1, v1[r] - mean1, d1);
+                    }
+                    run0 = chan_merge(run0, Stat{16.f, mean0, d0});
+                    run1 = chan_merge(run1, Stat{16.f, mean1, d1});
+                    continue;
+                }
+                int cnt = 0;
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
+                    cnt += in;
+                    s0 += in ? v0[r] : 0.f;
+                    s1 += in ? v1[r] : 0.f;
+                }
+                if (cnt > 0) {
+                    const float fn = (float)cnt, mean0 = s0 / fn, mean1 = s1 / fn;
+                    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
+                        d0 = in ? fmaf(v0[r] - mean0, v0[r] - mean0, d0) : d0;
+                        d1 = in ? fmaf(v1[r] - mean1, v1[r] - mean1, d1) : d1;
+                    }
+                    run0 = chan_merge(run0, Stat{fn, mean0, d0});
+                    run1 = chan_merge(run1, Stat{fn, mean1, d1});
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p0 = ts + 8 * j + 4 * kk;  // positions of registers 4j..4j+3
+                    mf4 z0 = mf4{acc0[4 * j], acc0[4 * j + 1], acc0[4 * j + 2], acc0[4 * j + 3]} + bias0;
+                    mf4 z1 = mf4{acc1[4 * j], acc1[4 * j + 1], acc1[4 * j + 2], acc1[4 * j + 3]} + bias1;
+                    if (MODE == kC8Apply) {
+                        z0 = (z0 * pm0 - mu0) * A0 + B0;
+                        z1 = (z1 * pm1 - mu1) * A1 + B1;
+                        if (e.clamp) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                z0[r] = fminf(fmaxf(z0[r], e.lo), e.hi);
+                                z1[r] = fminf(fmaxf(z1[r], e.lo), e.hi);
+                            }
+                        }
+                        z0 *= q0;
+                        z1 *= q1;
+                    }
+                    *reinterpret_cast<mf4*>(c0 + p0) = z0;
+                    *reinterpret_cast<mf4*>(c1 + p0) = z1;
+                }
+            }
+        }
+        if (more) drop(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    if (MODE == kC8Stats) {
+        // lane halves hold the same channels (lower half first), then the waves in order
+        Stat o0, o1;
+        o0.n = __shfl_xor(run0.n, 32);
+        o0.mean = __shfl_xor(run0.mean, 32);
+        o0.m2 = __shfl_xor(run0.m2, 32);
+        o1.n = __shfl_xor(run1.n, 32);
+        o1.mean = __shfl_xor(run1.mean, 32);
+        o1.m2 = __shfl_xor(run1.m2, 32);
+        run0 = kk ? chan_merge(o0, run0) : chan_merge(run0, o0);
+        run1 = kk ? chan_merge(o1, run1) : chan_merge(run1, o1);
+        Stat* red = reinterpret_cast<Stat*>(win);  // [wave][channel]; the windows are done
+        if (kk == 0) {
+            red[wave * kC8Cout + m] = run0;
+            red[wave * kC8Cout + 32 + m] = run1;
+        }
+        __syncthreads();
+        if (threadIdx.x < kC8Cout) {
+            Stat t = red[threadIdx.x];
+#pragma unroll
+            for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + threadIdx.x]);
+            e.part[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = float4{t.n, t.mean, t.m2, 0.f};
+        }
+    }
+}
+
+// Per-channel merge of the statistics pass's workgroup partials ([channel][workgroup]), one wave
+// per channel, in a fixed order (lanes stride the partials, then the fixed shuffle tree): the
+// channel's mean and 1/sqrt(biased var + eps), and the optional outputs of the batch-norm
+// entry points (saved statistics, running statistics with the unbiased variance).
+__global__ __launch_bounds__(kWave) void c8_stats_merge_kernel(const float4* __restrict__ part, int G,
+                                                                float eps, GroupStat* stats,
+                                                                RunningStats run)
+{
+    const int ch = blockIdx.x;
+    Stat st = stat_empty();
+    for (int i = (int)threadIdx.x; i < G; i += kWave) {
+        const float4 p = part[(int64_t)ch * G + i];
+        st = chan_merge(st, Stat{p.x, p.y, p.z});
+    }
+    st = wave_merge<kWave>(st);
+    if (threadIdx.x == 0) {
+        const float rstd = rsqrtf(st.m2 / st.n + eps);
+        stats[ch] = GroupStat{0.f, st.mean, rstd, 0.f};
+        if (run.mean) {
+            const float mo = run.momentum;
+            run.mean[ch] = (1.f - mo) * run.mean[ch] + mo * st.mean;
+            run.var[ch] = (1.f - mo) * run.var[ch] + mo * (st.m2 / (st.n - 1.f));
+        }
     }
 }
 
@@ -540,6 +877,12 @@ bool conv_valu_forced()
     return e && e[0] == 'v';  // "valu": the vector-ALU producer (comparisons)
 }
 
+bool conv_fp32_forced()
+{
+    const char* e = getenv("NORMRED_CONV");
+    return e && e[0] == 'f';  // "fp32": the 2-D producer on the fp32 matrix instruction
+}
+
 constexpr int kRingLdsMax = 64 * 1024;  // LDS bytes of one workgroup's ring
 
 // Ring geometry for the persistent producer; false when the shape does not fit (ring beyond
@@ -608,7 +951,51 @@ hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, co
     }
     return hipGetLastError();
 }
+
+constexpr int kC8B = 4;  // output rows per box of the 2-D matrix producer (2 measured ~8 % slower)
+
+// Persistent grid of the 2-D matrix producer: two workgroups per CU (one wave per SIMD each,
+// the most its VGPR use allows), at most one per box.
+int64_t c8_grid(const ConvGeom& g)
+{
+    int wgs = 2;
+    if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs = std::min(8, std::max(1, atoi(e)));
+    const int64_t nbox = (g.OH + kC8B - 1) / kC8B;
+    return std::min<int64_t>(std::min<int64_t>(g.N * nbox, (int64_t)device_cus() * wgs), kC8MaxGrid);
+}
 }  // namespace
+
+// 16-byte output stores need every box to start on a multiple of 4 positions: kC8B * 62 is,
+// and SP % 4 == 0 keeps planes aligned. SP % 4 == 0 also means an even output height, so every
+// box holds an even number of rows (at least 124 positions, a multiple of 4).
+bool conv2d_c8_shape(const ConvGeom& g)
+{
+    return !g.cl && g.dims == 2 && g.Cin == kC8Cin && g.Cout == kC8Cout && g.W == kC8W &&
+           g.SP % 4 == 0 && g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+}
+
+int64_t conv2d_c8_stats_grid(const ConvGeom& g) { return c8_grid(g); }
+
+bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out)
+{
+    return conv2d_c8_shape(g) && !conv_valu_forced() && !conv_fp32_forced() &&
+           (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+}
+
+hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
+                                     const float* b, float* out, C8Chain e, GroupStat* stats,
+                                     float eps, RunningStats run, hipStream_t stream)
+{
+    const int64_t G = c8_grid(g);
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Stats><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    c8_stats_merge_kernel<<<dim3((unsigned)g.Cout), dim3(kWave), 0, stream>>>(e.part, (int)G, eps, stats, run);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    e.stats = stats;
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    return hipGetLastError();
+}
 
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream)
@@ -619,16 +1006,15 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
     ConvRing rg;
     if (!conv_valu_forced() && small) {
         // 16-byte output stores need every box to start on a multiple of 4 positions: B * 62
-        // is, SP % 4 == 0 keeps planes aligned
-        if (!g.cl && g.dims == 2 && g.Cin == 8 && g.Cout == 64 && g.W == kC8W && (uintptr_t)x % 16 == 0 &&
-            (uintptr_t)c % 16 == 0 && g.SP % 4 == 0) {
-            const int cus = device_cus();
-            int wgs = 2;  // per CU: one wave per SIMD each, the most its VGPR use allows
-            if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs = std::max(1, atoi(e));
-            constexpr int B = 4;  // output rows per box (2 rows measured ~8 % slower)
-            const int64_t nbox = (g.OH + B - 1) / B;
-            const int64_t grid = std::min<int64_t>(g.N * nbox, (int64_t)cus * wgs);
-            conv2d_c8_mfma32_kernel<B><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(g, x, w, b, c);
+        // is, SP % 4 == 0 keeps planes aligned. SP % 4 == 0 also means an even output height,
+        // so every box holds an even number of rows (at least 124 positions, a multiple of 4)
+        if (conv2d_c8_shape(g) && (uintptr_t)x % 16 == 0 && (uintptr_t)c % 16 == 0) {
+            const int64_t grid = c8_grid(g);
+            if (conv_fp32_forced())
+                conv2d_c8_mfma32_kernel<kC8B><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(g, x, w, b, c);
+            else
+                conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+                    g, x, w, b, c, C8Chain{});
             return hipGetLastError();
         }
         if (g.dims == 2 && g.Cin == 8 && g.Cout == 64 && make_ring(g, x, c, 1, &rg))

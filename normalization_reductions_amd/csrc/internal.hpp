@@ -82,6 +82,35 @@ struct ConvRing {
     int vec_out;    // 16-byte output stores (aligned groups of 4 positions)
 };
 
+// Epilogue and statistics arguments of the 2-D C_in 8 -> C_out 64 matrix producer when it runs
+// a batch-norm chain by recomputation (statistics pass, merge, apply pass).
+struct C8Chain {
+    const float* pre_mul = nullptr;
+    float4* part = nullptr;         // statistics pass: [C_out][workgroups] (count, mean, M2, -)
+    const GroupStat* stats = nullptr;  // apply pass: per channel
+    const float* gamma = nullptr;
+    const float* beta = nullptr;
+    float out_scale = 1.f;
+    int clamp = 0;
+    float lo = 0.f, hi = 0.f;
+    const float* post_mul = nullptr;
+};
+
+// The 2-D C_in 8 -> C_out 64, W = 64 shapes of the matrix producer (pointer alignment aside):
+// even output heights, int32 offsets within a batch item.
+bool conv2d_c8_shape(const ConvGeom& g);
+// Workgroups of its statistics pass (the number of partials per channel); at most kC8MaxGrid.
+constexpr int64_t kC8MaxGrid = 4096;
+int64_t conv2d_c8_stats_grid(const ConvGeom& g);
+// Whether a batch-norm chain of this shape and these pointers runs by recomputation (the
+// bf16x6 producer is not overridden for comparisons).
+bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out);
+// Batch-norm chain by recomputation: statistics pass into e.part, fixed-order merge into
+// stats (and the running statistics), then the conv again with the chain epilogue into out.
+// Needs conv2d_c8_shape(g) and 16-byte aligned x and out.
+hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
+                                     const float* b, float* out, C8Chain e, GroupStat* stats,
+                                     float eps, RunningStats run, hipStream_t stream);
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream);
 

@@ -547,6 +547,10 @@ CHAIN_CASES = [
     ((3, 8, 9, 64), 64, True, False, True),
     ((5, 8, 17, 64), 64, False, False, True),
     ((2, 8, 6, 64), 64, True, True, True),
+    # the 2-D matrix producer with whole boxes of 4 output rows (even output heights): boxes of
+    # 4, 4, 2 rows; instance statistics with the max over channels
+    ((3, 8, 12, 64), 64, True, False, True),
+    ((2, 8, 10, 64), 64, False, True, True),
 ]
 
 
@@ -578,9 +582,11 @@ def test_conv_chain_general(dev, nra, orc, shape, cout, batch, red, full):
 
 CHAIN_RUNNING_CASES = [
     # (x shape, Cout, reduce_max_c): split path, pipelined in place, one workgroup per channel,
-    # max over channels, and the 2-D matrix-core producer shape
+    # max over channels, the 2-D ring producer shape, and the 64-wide matrix producer
     ((2, 8, 15, 13), 64, False), ((40, 2, 42, 42), 4, False), ((9, 2, 40, 42), 6, False),
     ((3, 1, 5, 6, 7), 20, True), ((3, 8, 20, 22), 64, False),
+    # the 2-D 64-wide matrix producer with even output height: batch norm by recomputation
+    ((3, 8, 12, 64), 64, False),
 ]
 
 
@@ -740,6 +746,45 @@ def test_conv_vector_alu_producer(dev, nra, orc, monkeypatch):
     ref = orc.conv_norm_epilogue(inp["x"][:16], inp["w"], inp["b"], batch=False,
                                  pre_mul=inp["mult"], clamp=inp["clamp"], post_mul=inp["mult"],
                                  reduce_max_c=True)
+    assert maxerr(H(out), ref) <= TOL
+
+
+@pytest.mark.parametrize("mode", ["bf16x6", "fp32"])
+def test_conv2d_matrix_producer_fp32_accuracy(dev, nra, orc, monkeypatch, mode):
+    # The 2-D C_in 8 -> C_out 64 producer read through the eval entry point with an identity
+    # fold (running mean 0, running variance 1, eps 0, no affine: W and b pass unchanged), so
+    # the output is the conv itself. Both matrix forms must be fp32-accurate element by
+    # element: |conv - fp64 conv| <= 2^-20 (sum |x||w| + |b|). The default splits every value
+    # into three bf16 parts (six partial products); a two-part split would leave errors near
+    # 4e-6 of that sum and fail. "fp32" selects the fp32 matrix instruction.
+    if mode == "fp32":
+        monkeypatch.setenv("NORMRED_CONV", "fp32")
+    g = np.random.Generator(np.random.PCG64(7272))
+    x = (g.standard_normal((3, 8, 20, 64)) * 3).astype(np.float32)  # 18 output rows: last box of 2
+    bound = 1 / np.sqrt(72)
+    w = g.uniform(-bound, bound, (64, 8, 3, 3)).astype(np.float32)
+    b = g.uniform(-bound, bound, 64).astype(np.float32)
+    t = lambda a: T(a, dev)
+    out = nra.conv_bn_eval_forward(t(x), t(w), t(b), t(np.zeros(64, np.float32)),
+                                   t(np.ones(64, np.float32)), eps=0.0)
+    ref = orc.conv_k3(x, w, b)
+    den = orc.conv_k3(np.abs(x), np.abs(w), np.abs(b))
+    ratio = float(np.max(np.abs(H(out).astype(np.float64) - ref) / den))
+    _log("conv2d producer %s: max |err| / (sum|x||w| + |b|) = %.3e" % (mode, ratio))
+    assert ratio <= 2.0 ** -20
+
+
+def test_conv2d_fp32_matrix_producer_chain(dev, nra, orc, monkeypatch):
+    # the fp32-instruction form of the 2-D producer through the batch-norm chain
+    monkeypatch.setenv("NORMRED_CONV", "fp32")
+    inp = synth.host_inputs(4)
+    t = lambda a: T(a, dev)
+    x = np.ascontiguousarray(inp["x"][:8])
+    out = nra.conv_norm_epilogue_forward(t(x), t(inp["w"]), t(inp["b"]),
+                                         norm=nra.NR_NORM_BATCH_TRAIN, gamma=t(inp["gamma"]),
+                                         beta=t(inp["beta"]), out_scale=2.0)
+    ref = orc.conv_norm_epilogue(x, inp["w"], inp["b"], batch=True, gamma=inp["gamma"],
+                                 beta=inp["beta"], out_scale=2.0)
     assert maxerr(H(out), ref) <= TOL
 
 
