@@ -188,8 +188,17 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
     };
 
     // This lane's B fragment (channel ch, taps 4s + q): weight, outer tap a (kd in 3-D, kh in
-    // 2-D) and the offset of the tap inside one slot, packed as (a << 24) | offset.
+    // 2-D) and the offset of the tap inside one slot, packed as (a << 24) | offset. W is read
+    // once per workgroup with coalesced loads into the ring (free until the first window is
+    // staged) and the lanes take their values from there: per-lane gathers would touch a cache
+    // line per lane and load, and registers still awaiting a global load at the step loop make
+    // the compiler wait for all loads in flight -- the next slice's prefetch included -- before
+    // the tile loop.
     const int ch = wn * 16 + r16;
+    const int wcount = (int)g.Cout * K;  // the launcher sizes the ring to hold W and the bias
+    for (int i = (int)threadIdx.x; i < wcount; i += kMfmaBlock) ring[i] = w[i];
+    for (int i = (int)threadIdx.x; i < (int)g.Cout; i += kMfmaBlock) ring[wcount + i] = b ? b[i] : 0.f;
+    __syncthreads();
     int tap[KS];
     float bw[KS];
 #pragma unroll
@@ -208,13 +217,14 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
         }
         const int lds_off = CL ? in_off * Cin + ci : ci * rg.inner_in + in_off;
         tap[s] = valid ? (a << 24) | lds_off : 0;
-        bw[s] = valid ? w[(int64_t)ch * K + k] : 0.f;
+        bw[s] = valid ? ring[ch * K + k] : 0.f;
     }
     // accumulator start: the bias of the channel(s) a lane's 4 results belong to (planar: its
     // channel ch at 4 positions; channels last: channels 4q..4q+3 of its tile at one position)
     mf4 bias4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bias4[r] = b ? b[CL ? wn * 16 + 4 * q + r : ch] : 0.f;
+    for (int r = 0; r < 4; ++r) bias4[r] = ring[wcount + (CL ? wn * 16 + 4 * q + r : ch)];
+    __syncthreads();
 
     const int64_t total = (int64_t)g.N * rg.OO * rg.T;
     const int64_t begin = total * blockIdx.x / gridDim.x;
@@ -935,7 +945,9 @@ template <int DIMS, int KS, int WAVES_N, int MT, int PF>
 hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, const float* x,
                        const float* w, const float* b, float* c, hipStream_t stream)
 {
-    const size_t lds = 4 * (size_t)g.Cin * rg.inner_in * sizeof(float);
+    // the ring, which first holds W (C_out x K floats) and the bias while the lanes take theirs
+    const size_t lds = std::max<size_t>(4 * (size_t)g.Cin * rg.inner_in,
+                                        (size_t)g.Cout * (g.Cin * (DIMS == 3 ? 27 : 9) + 1)) * sizeof(float);
     const int grid = ring_grid(g, rg, wgs_per_cu);
     const dim3 gd(grid), bd(kMfmaBlock);
     if (g.cl) {
