@@ -613,8 +613,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int64_t n = box / nbox;
         const int o0 = (int)(box - n * nbox) * B;
         const int BP = min(B, OH - o0) * OW;  // positions in this box: a multiple of 4, >= 62
-        float* c0 = c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
-        float* c1 = c0 + 32 * g.SP;
+        float* c0 = MODE == kC8Stats ? nullptr : c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
+        float* c1 = MODE == kC8Stats ? nullptr : c0 + 32 * g.SP;
         // exactly two tiles per wave, each 32 whole positions of the box: the last tile ends at
         // the box's last position (overlapping the one before), and waves with no tile left
         // repeat the last. Overlaps rewrite bitwise-identical values, and every lane issues the

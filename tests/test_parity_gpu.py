@@ -788,6 +788,39 @@ def test_conv2d_fp32_matrix_producer_chain(dev, nra, orc, monkeypatch):
     assert maxerr(H(out), ref) <= TOL
 
 
+@pytest.mark.parametrize("shape,misalign", [((1, 8, 4, 64), False), ((3, 8, 18, 64), True)])
+def test_conv2d_bn_recompute_edges(dev, nra, orc, shape, misalign):
+    # batch norm on the 2-D matrix producer's shape: a single box of two output rows (waves
+    # repeat the last tile, whose positions must count once in the statistics), and an x four
+    # bytes off 16-byte alignment, which the producer cannot take (the in-place plan runs)
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(4242 + shape[2]))
+    x = (g.standard_normal(shape) * 2 + 0.5).astype(np.float32)
+    w = (g.standard_normal((64, 8, 3, 3)) * 0.2).astype(np.float32)
+    b = g.standard_normal(64).astype(np.float32)
+    rm0 = g.uniform(-1, 1, 64).astype(np.float32)
+    rv0 = g.uniform(0.5, 2, 64).astype(np.float32)
+    if misalign:
+        buf = torch.empty(x.size + 1, dtype=torch.float32, device=dev)
+        xt = buf[1:].view(shape)
+        xt.copy_(torch.from_numpy(x))
+        assert xt.data_ptr() % 16 != 0
+    else:
+        xt = T(x, dev)
+    rm, rv = T(rm0, dev), T(rv0, dev)
+    out = nra.conv_norm_epilogue_forward(xt, T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN,
+                                         running_mean=rm, running_var=rv, momentum=0.5)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=True)
+    err = maxerr(H(out), ref)
+    _log("conv2d bn %s misaligned %s: max_abs_err %.3e" % (shape, misalign, err))
+    assert err <= TOL
+    c = orc.conv_k3(x, w, b)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    rm_ref, rv_ref = orc.bn_running_update(mean, var, c.size // 64, rm0, rv0, momentum=0.5)
+    _check_running(rm, rv, rm_ref, rv_ref, "conv2d bn %s" % (shape,))
+
+
 def test_graph_capture_and_replay(dev, nra, orc):
     # every launch of these entry points can be captured: no hipMemsetAsync (fill kernels
     # instead), no synchronization, regular launches. Capture instance norm (read-once
