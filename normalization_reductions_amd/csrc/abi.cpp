@@ -635,7 +635,7 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
     hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_partial(L.sg, c, d->pre_mul, partials, stream);
+    e = launch_split_partial(L.sg, c, d->pre_mul, partials, stream, true);
     if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_split_merge(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr,
                            RunningStats{d->running_mean, d->running_var, d->momentum}, stream);

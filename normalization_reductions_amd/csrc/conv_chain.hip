@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_vec_kernel(ChainArgs 
         const float A = s.rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale;
         const float B = (a.beta ? a.beta[k] : 0.f) * a.out_scale;
         const float qm = a.post_mul ? a.post_mul[k] : 1.f;
-        const f4 cv = ld_stream(cp + k * plane4);
+        const f4 cv = cp[k * plane4];  // plain load: the statistics pass just read these lines
         f4 z = ((cv * pm - s.pivot) - s.mean_d) * A + B;
         if (a.clamp) {
             z.x = fminf(fmaxf(z.x, a.lo), a.hi);
@@ -866,14 +866,14 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_kernel(ChainArgs a)
     if (a.reduce_max_c) {
         float m = -INFINITY;
         for (int64_t k = 0; k < a.Cout; ++k) {
-            const float v = chain_value(a, n, k, ld_stream1(a.c + (n * a.Cout + k) * a.SP + i));
+            const float v = chain_value(a, n, k, a.c[(n * a.Cout + k) * a.SP + i]);
             m = fmaxf(m, v);
         }
         a.out[n * a.SP + i] = m;
     } else {
         for (int64_t k = 0; k < a.Cout; ++k) {
             const int64_t o = (n * a.Cout + k) * a.SP + i;
-            a.out[o] = chain_value(a, n, k, ld_stream1(a.c + o));
+            a.out[o] = chain_value(a, n, k, a.c[o]);
         }
     }
 }

@@ -43,8 +43,10 @@ struct GroupStat {    // per group, written by the merge step
 
 SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec);
 
+// cached: plain loads (a chain's conv output, read again by the epilogue right after);
+// otherwise streaming loads.
 hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
-                                float2* partials, hipStream_t stream);
+                                float2* partials, hipStream_t stream, bool cached = false);
 struct RunningStats {      // optional in-place running-statistics update (batch groups)
     float* mean = nullptr;
     float* var = nullptr;
