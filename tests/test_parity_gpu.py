@@ -551,6 +551,9 @@ CHAIN_CASES = [
     # 4, 4, 2 rows; instance statistics with the max over channels
     ((3, 8, 12, 64), 64, True, False, True),
     ((2, 8, 10, 64), 64, False, True, True),
+    # instance statistics and the max over 16 channels on 2-D shapes: 1596 and 16384 positions
+    ((3, 4, 40, 44), 16, False, True, True),
+    ((2, 2, 130, 130), 16, False, True, False),
 ]
 
 
@@ -819,6 +822,24 @@ def test_conv2d_bn_recompute_edges(dev, nra, orc, shape, misalign):
     _, mean, var = orc.batch_norm_train(c, with_stats=True)
     rm_ref, rv_ref = orc.bn_running_update(mean, var, c.size // 64, rm0, rv0, momentum=0.5)
     _check_running(rm, rv, rm_ref, rv_ref, "conv2d bn %s" % (shape,))
+
+
+def test_conv_chain_max_c_misaligned_out(dev, nra, orc):
+    # an `out` four bytes off 16-byte alignment: the epilogue takes its scalar path
+    import torch
+
+    i5 = synth.host_inputs(5)
+    x = np.ascontiguousarray(i5["x"][:2])
+    t = lambda a: T(a, dev)
+    buf = torch.empty(2 * 14 * 30 * 30 + 1, dtype=torch.float32, device=dev)
+    out = buf[1:].view(2, 14, 30, 30)
+    assert out.data_ptr() % 16 != 0
+    nra.conv_norm_epilogue_forward(t(x), t(i5["w"]), t(i5["b"]), out=out, norm=nra.NR_NORM_INSTANCE,
+                                   pre_mul=t(i5["mult"]), clamp=(-1.0, 1.0), post_mul=t(i5["mult"]),
+                                   reduce_max_c=True)
+    ref = orc.conv_norm_epilogue(x, i5["w"], i5["b"], batch=False, pre_mul=i5["mult"],
+                                 clamp=(-1.0, 1.0), post_mul=i5["mult"], reduce_max_c=True)
+    assert maxerr(H(out), ref) <= TOL
 
 
 def test_graph_capture_and_replay(dev, nra, orc):
