@@ -492,20 +492,34 @@ __device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsign
 // for batch-norm statistics; kC8Apply recomputes the conv and stores the normalized chain
 // output ((v - mean) * rstd * gamma + beta) * out_scale, clamped, times post_mul, in the order
 // the chain epilogue uses.
+//
+// For channels of at least kC8StatsTwoParts values the statistics pass splits x into two
+// parts and forms hh, hm, mh and x_h w_l (four products for six): each conv value is then off
+// by up to ~3e-5 of its scale, but that error comes from the rounding of x, which varies from
+// position to position and averages out of a channel's mean and variance (emulated on the CPU
+// and measured: ~2e-7 relative, at the rounding of the fp32 sums). W keeps three parts: its
+// rounding error would be the same at every position and would bias the variance (by ~2e-6
+// with two parts). Smaller channels, where too few values average, use all six products.
+constexpr int64_t kC8StatsTwoParts = 16384;
 enum { kC8Conv = 0, kC8Stats = 1, kC8Apply = 2 };
 
-template <int B, int MODE>
+template <int B, int MODE, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const float* __restrict__ w,
                              const float* __restrict__ b, float* __restrict__ c, C8Chain e)
 {
     constexpr int W = kC8W, OW = W - 2;
+    // NS: bf16 parts of each x value in the staged windows. Three (products hh, hm, mh, mm, hl,
+    // lh: fp32 accuracy) wherever conv values are stored; two (products hh, hm, mh and x_h w_l)
+    // for the statistics of large channels. W always has three.
+    static_assert(NS == 3 || (NS == 2 && MODE == kC8Stats), "two parts only for statistics");
     constexpr int ROWS = B + 2;                    // input rows a box reads
     constexpr int SPLIT = ROWS * W * kC8Cin;       // bf16 of one split of a staged window
-    constexpr int WIN = 3 * SPLIT;                 // bf16 of one staged window
+    constexpr int WIN = NS * SPLIT;                // bf16 of one staged window
+    constexpr int WSTAGE = 2 * kBfChunks * 3 * 64 * 8;  // bf16 of the staged B operands
     constexpr int ITEMS = ROWS * (W / 4) * 2;      // staging items: row x 4 columns x 4 channels
     static_assert(ITEMS <= 256, "one staging item per thread");
-    __shared__ __attribute__((aligned(16))) unsigned short win[2 * WIN];
+    __shared__ __attribute__((aligned(16))) unsigned short win[2 * WIN > WSTAGE ? 2 * WIN : WSTAGE];
     const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = l & 31, kk = l >> 5;
     const int OH = (int)g.OH;
@@ -514,10 +528,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 
     // B operands: lane l holds W[n][0..7][tap 2q + l/32] for n = 32 nt + l%32, in three splits.
     // The workgroup reads W once with coalesced loads, splits each value, and lays the splits
-    // out in LDS as [nt][q][split][lane] x 8 bf16, from where every lane takes its 30 operands
+    // out in LDS as [nt][q][split][lane] x 8 bf16, from where every lane takes its operands
     // with 16-byte reads (gathering them per lane touched a cache line per lane and load).
     // The window buffers hold them until the first window is staged.
-    static_assert(2 * kBfChunks * 3 * 64 * 8 <= 2 * WIN, "operand staging fits the window buffers");
     static_assert(4 * kC8Cout * sizeof(Stat) <= 2 * WIN * sizeof(unsigned short), "partials fit");
     for (int i = (int)threadIdx.x; i < 2 * 3 * 32; i += 256) {  // the padding tap's operands
         const int nt = i / 96, sp = (i / 32) % 3, lane = 32 + i % 32;
@@ -592,7 +605,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 unsigned short* d = win + buf * WIN + (srow * W + 4 * sj + e) * kC8Cin + 4 * scq;
                 *reinterpret_cast<mu2*>(d) = mu2{h[0] | h[1] << 16, h[2] | h[3] << 16};
                 *reinterpret_cast<mu2*>(d + SPLIT) = mu2{mm[0] | mm[1] << 16, mm[2] | mm[3] << 16};
-                *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
+                if (NS == 3)
+                    *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
             }
         }
     };
@@ -638,13 +652,15 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 const unsigned short* a = q == 1 ? a2 : q == 4 ? a0 : a1;
                 const bf8 ah = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off));
                 const bf8 am = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + SPLIT));
-                const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + 2 * SPLIT));
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][1], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][1], acc1, 0, 0, 0);
+                if (NS == 3) {
+                    const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + (NS - 1) * SPLIT));
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][1], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][1], acc1, 0, 0, 0);
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[0][q][0], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[1][q][0], acc1, 0, 0, 0);
+                }
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][2], acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][2], acc1, 0, 0, 0);
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[0][q][0], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[1][q][0], acc1, 0, 0, 0);
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][1], acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][1], acc1, 0, 0, 0);
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][0], acc0, 0, 0, 0);
@@ -999,13 +1015,16 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
                                      float eps, RunningStats run, hipStream_t stream)
 {
     const int64_t G = c8_grid(g);
-    conv2d_c8_bf16x6_kernel<kC8B, kC8Stats><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
+    if (g.N * g.SP >= kC8StatsTwoParts)
+        conv2d_c8_bf16x6_kernel<kC8B, kC8Stats, 2><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
+    else
+        conv2d_c8_bf16x6_kernel<kC8B, kC8Stats, 3><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     c8_stats_merge_kernel<<<dim3((unsigned)g.Cout), dim3(kWave), 0, stream>>>(e.part, (int)G, eps, stats, run);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     e.stats = stats;
-    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply, 3><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
     return hipGetLastError();
 }
 
@@ -1025,7 +1044,7 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
             if (conv_fp32_forced())
                 conv2d_c8_mfma32_kernel<kC8B><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(g, x, w, b, c);
             else
-                conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+                conv2d_c8_bf16x6_kernel<kC8B, kC8Conv, 3><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
                     g, x, w, b, c, C8Chain{});
             return hipGetLastError();
         }

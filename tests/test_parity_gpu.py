@@ -824,6 +824,34 @@ def test_conv2d_bn_recompute_edges(dev, nra, orc, shape, misalign):
     _check_running(rm, rv, rm_ref, rv_ref, "conv2d bn %s" % (shape,))
 
 
+def test_conv2d_bn_recompute_statistics_accuracy(dev, nra, orc):
+    # The recomputing batch-norm chain takes the statistics of channels with >= 16384 values
+    # from a conv with four bf16 partial products (x in two parts, W in three): each value is
+    # up to ~3e-5 of its scale off, from the rounding of x, which averages out. With momentum 1
+    # the running buffers receive the batch mean and unbiased variance themselves; they must
+    # match the fp64 oracle to 1e-6 (of the channel's std for the mean, relative for the
+    # variance). W in two parts biases the variance by ~1.9e-6 (measured), a one-product conv
+    # by ~4e-6.
+    g = np.random.Generator(np.random.PCG64(8080))
+    x = g.standard_normal((16, 8, 64, 64)).astype(np.float32)
+    bound = 1 / np.sqrt(72)
+    w = g.uniform(-bound, bound, (64, 8, 3, 3)).astype(np.float32)
+    b = g.uniform(-bound, bound, 64).astype(np.float32)
+    rm = T(np.zeros(64, np.float32), dev)
+    rv = T(np.ones(64, np.float32), dev)
+    nra.conv_norm_epilogue_forward(T(x, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN,
+                                   running_mean=rm, running_var=rv, momentum=1.0)
+    c = orc.conv_k3(x, w, b)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    count = c.size // 64
+    var_u = var * count / (count - 1)
+    em = float(np.max(np.abs(H(rm) - mean) / np.sqrt(var)))
+    ev = float(np.max(np.abs(H(rv) - var_u) / var_u))
+    _log("recompute statistics: mean err / std %.3e, var rel err %.3e" % (em, ev))
+    assert em <= 1e-6
+    assert ev <= 1e-6
+
+
 def test_conv_chain_max_c_misaligned_out(dev, nra, orc):
     # an `out` four bytes off 16-byte alignment: the epilogue takes its scalar path
     import torch
