@@ -155,6 +155,15 @@ nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, in
  * groups fit the read-once kernels), the conv writes straight into `out`, which is then
  * normalized in place: `out` must be 16-byte aligned (else NR_ERR_MISALIGNED) and the workspace
  * holds only exchange slots. Otherwise the conv output is staged in the workspace.
+ * Batch norm on the 2-D shape C_in 8 -> C_out 64 with in_w = 64 and an even output height (the
+ * BN page's model) runs the conv twice instead, when x and out are 16-byte aligned: a
+ * statistics pass, then the conv again with the epilogue, so that c never goes to memory (the
+ * workspace holds per-workgroup partial statistics, at most 4 MiB); with other pointers the
+ * in-place plan above runs.
+ * Precision: the conv is fp32-accurate. On that 2-D shape its products come from exact
+ * three-part bf16 splits of x and w (six partial products; each part left out is below
+ * 2^-24 |x w|), and the statistics of channels of at least 16384 values use four partial
+ * products (x in two parts), whose per-value error averages out of the mean and variance.
  *
  * Channels last (channels_last = 1; IN3d page, its note on an (N, spatial, C) layout that makes
  * the max over channels contiguous): x is [N, (D,) H, W, C_in] and out is
