@@ -212,9 +212,8 @@ nr_status run_split(const SplitGeom& g, const float* x, float* y, float eps, con
     if (g.slices * g.chunks > 0x7fffffffLL)
         return fail(NR_ERR_UNSUPPORTED, "%s: %lld slices x %lld chunks exceed one launch", fn,
                     (long long)g.slices, (long long)g.chunks);
-    hipError_t e = launch_split_partial(g, x, nullptr, partials, stream);
-    if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_merge(g, x, nullptr, partials, eps, stats, save_mean, save_invstd, run, stream);
+    hipError_t e = launch_split_stats(g, x, nullptr, partials, eps, stats, save_mean, save_invstd,
+                                      run, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_split_apply(g, x, y, stats, gamma, beta, out_scale, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
@@ -635,10 +634,8 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
     hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_partial(L.sg, c, d->pre_mul, partials, stream, true);
-    if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_merge(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr,
-                           RunningStats{d->running_mean, d->running_var, d->momentum}, stream);
+    e = launch_split_stats(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr,
+                           RunningStats{d->running_mean, d->running_var, d->momentum}, stream, true);
     if (e != hipSuccess) return hip_fail(e, fn);
     ChainArgs a;
     a.c = c;

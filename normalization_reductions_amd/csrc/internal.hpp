@@ -43,20 +43,20 @@ struct GroupStat {    // per group, written by the merge step
 
 SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec);
 
-// cached: plain loads (a chain's conv output, read again by the epilogue right after);
-// otherwise streaming loads.
-hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
-                                float2* partials, hipStream_t stream, bool cached = false);
+
 struct RunningStats {      // optional in-place running-statistics update (batch groups)
     float* mean = nullptr;
     float* var = nullptr;
     float momentum = 0.f;
 };
 
-hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
-                              const float2* partials, float eps, GroupStat* stats,
-                              float* save_mean, float* save_invstd, RunningStats run,
-                              hipStream_t stream);
+// Group statistics: partials per (slice, chunk), then the fixed-order merge; instance groups of
+// one chunk write their statistics directly. cached: plain loads (a chain's conv output, read
+// again by the epilogue right after); otherwise streaming loads.
+hipError_t launch_split_stats(const SplitGeom& g, const float* x, const float* pre_mul,
+                              float2* partials, float eps, GroupStat* stats, float* save_mean,
+                              float* save_invstd, RunningStats run, hipStream_t stream,
+                              bool cached = false);
 hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
                               const GroupStat* stats, const float* gamma, const float* beta,
                               float out_scale, hipStream_t stream);

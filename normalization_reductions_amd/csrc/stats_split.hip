@@ -59,10 +59,15 @@ __device__ __forceinline__ Stat fold16(Stat run, const float (&d)[16], int n)
 
 // CACHED: plain loads instead of streaming ones, for a chain's conv output that the epilogue
 // reads again right after (measured: the epilogue pass 20.8 -> 17.0 us on the IN3d workload).
-template <bool VEC, bool CACHED>
+// FINAL: instance groups of one chunk, whose partial is the group's statistics: write them as
+// the merge step would (same arithmetic: merging one partial with empty ones changes nothing)
+// and skip the merge launch.
+template <bool VEC, bool CACHED, bool FINAL>
 __global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, const float* x,
                                                                const float* pre_mul,
-                                                               float2* partials)
+                                                               float2* partials, float eps,
+                                                               GroupStat* stats, float* save_mean,
+                                                               float* save_invstd)
 {
     __shared__ Stat wstat[kNW];
     const int64_t wg = blockIdx.x;
@@ -120,7 +125,16 @@ __global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, cons
     if (tid < kWave) {
         Stat w = tid < kNW ? wstat[tid] : stat_empty();
         w = wave_merge<kNW>(w);
-        if (tid == 0) partials[wg] = make_float2(w.mean, w.m2);
+        if (tid == 0) {
+            if (FINAL) {
+                const float rstd = rsqrtf(w.m2 / w.n + eps);
+                stats[slice] = GroupStat{K, w.mean, rstd, 0.f};
+                if (save_mean) save_mean[slice] = K + w.mean;
+                if (save_invstd) save_invstd[slice] = rstd;
+            } else {
+                partials[wg] = make_float2(w.mean, w.m2);
+            }
+        }
     }
 }
 
@@ -233,20 +247,22 @@ SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec)
     return g;
 }
 
-hipError_t launch_split_partial(const SplitGeom& g, const float* x, const float* pre_mul,
-                                float2* partials, hipStream_t stream, bool cached)
+namespace {
+template <bool FINAL>
+void launch_partial(const SplitGeom& g, const float* x, const float* pre_mul, float2* partials,
+                    float eps, GroupStat* stats, float* save_mean, float* save_invstd,
+                    hipStream_t stream, bool cached)
 {
     const int64_t grid = g.slices * g.chunks;
     const dim3 gd((unsigned)grid), bd(kBlock);
     if (g.vec && cached)
-        split_partial_kernel<true, true><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials);
+        split_partial_kernel<true, true, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
     else if (g.vec)
-        split_partial_kernel<true, false><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials);
+        split_partial_kernel<true, false, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
     else if (cached)
-        split_partial_kernel<false, true><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials);
+        split_partial_kernel<false, true, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
     else
-        split_partial_kernel<false, false><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials);
-    return hipGetLastError();
+        split_partial_kernel<false, false, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd);
 }
 
 hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* pre_mul,
@@ -258,6 +274,21 @@ hipError_t launch_split_merge(const SplitGeom& g, const float* x, const float* p
     split_merge_kernel<<<dim3((unsigned)groups), dim3(kWave), 0, stream>>>(
         g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, run);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_split_stats(const SplitGeom& g, const float* x, const float* pre_mul,
+                              float2* partials, float eps, GroupStat* stats, float* save_mean,
+                              float* save_invstd, RunningStats run, hipStream_t stream, bool cached)
+{
+    if (!g.batch && g.chunks == 1) {  // every group is one chunk: no merge step
+        launch_partial<true>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, stream, cached);
+        return hipGetLastError();
+    }
+    launch_partial<false>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, stream, cached);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_merge(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, run, stream);
 }
 
 hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
