@@ -619,8 +619,10 @@ def test_conv_chain_running_statistics(dev, nra, orc, shape, cout, red):
 
 
 # eval-mode batch norm folded into the conv: the two model shapes, plus ragged small cases
+# ((3, 8, 10, 64): the 2-D matrix producer with an even output height)
 CONV_EVAL_CASES = [((128, 8, 64, 64), 64), ((128, 3, 16, 32, 32), 16), ((2, 3, 9, 11), 5),
-                   ((3, 2, 5, 6, 7), 17), ((1, 8, 15, 13), 64), ((7, 8, 13, 64), 64)]
+                   ((3, 2, 5, 6, 7), 17), ((1, 8, 15, 13), 64), ((7, 8, 13, 64), 64),
+                   ((3, 8, 10, 64), 64)]
 
 
 @pytest.mark.parametrize("shape,cout", CONV_EVAL_CASES)
