@@ -205,6 +205,10 @@ def extras(torch, nra, x, y, steps, warmup):
     tot, per, med = time_calls(lambda: nra.stream_copy(x, y), steps, warmup, torch)
     out["copy_ceiling_GBps"] = round(MIN_BYTES / (per / 1e3) / 1e9, 1)
     log("stream copy of the same bytes: %.3f ms -> %.1f GB/s" % (per, out["copy_ceiling_GBps"]))
+    # the runtime's own device-to-device copy of the same bytes (torch's copy_), for comparison
+    tot, per, med = time_calls(lambda: y.copy_(x), steps, warmup, torch)
+    out["runtime_copy_GBps"] = round(MIN_BYTES / (per / 1e3) / 1e9, 1)
+    log("runtime device copy of the same bytes: %.3f ms -> %.1f GB/s" % (per, out["runtime_copy_GBps"]))
     # the same workload through the two-pass streaming variant
     tot, per, med = time_calls(lambda: nra.inorm_forward(x, y, variant=nra.NR_VARIANT_SPLIT),
                                steps, warmup, torch)
