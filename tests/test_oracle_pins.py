@@ -143,6 +143,25 @@ def test_in_cancellation_workload_matches_torch(oracle_mod):
     np.testing.assert_allclose(y, ref, rtol=0, atol=2e-6)
 
 
+def test_in_slices_form_matches_torch_float64(oracle_mod):
+    # the [count, S] form the sampled full-size checks use: each row normalized on its own
+    # (torch's float64 instance norm over a [1, count, S] view), ragged S, returned statistics
+    import torch
+    import torch.nn.functional as F
+
+    g = np.random.Generator(np.random.PCG64(31))
+    for S in (1, 7, 1000, 4099):
+        xs = (g.standard_normal((5, S)) * g.uniform(0.1, 10, (5, 1)) + g.uniform(-50, 50, (5, 1))).astype(np.float32)
+        y, mean, var = oracle_mod.instance_norm_slices(xs, with_stats=True)
+        if S == 1:  # one value per slice: y = 0 (torch refuses the shape)
+            ref = np.zeros_like(xs)
+        else:
+            ref = F.instance_norm(torch.from_numpy(xs).double()[None], eps=1e-5)[0].numpy()
+        np.testing.assert_allclose(y, ref, rtol=0, atol=2e-6)
+        np.testing.assert_allclose(mean, xs.astype(np.float64).mean(axis=1), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(var, xs.astype(np.float64).var(axis=1), rtol=1e-10, atol=1e-12)
+
+
 def test_in_naive_sum_of_squares_fails_on_cancellation_workload(oracle_mod):
     # IN2d page, its numerics discussion: sum and sum of squares in fp32 lose the variance to
     # cancellation. On the offset/spread workload that shortcut misses the 1e-4 bar while
