@@ -303,6 +303,44 @@ def extras(torch, nra, x, y, steps, warmup):
     return out
 
 
+def conv_producers(steps, warmup):
+    """The conv producers alone on the two model shapes (the eval entry point with running mean
+    0, running variance 1, eps 0: W and b pass unchanged), each producer selected by the
+    library's NORMRED_CONV override: the vector-ALU direct kernel against the matrix-core
+    ones. Prints one JSON line of median ms per call (HIP events, a 512 MB read before each)."""
+    import numpy as np
+    import torch
+
+    import normalization_reductions_amd as nra
+    import synth
+
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    res = {"metric": "conv producer time, ms (median per call)", "shapes": {}}
+    for wl, name, cout, oshape in ((4, "conv2d 8->64 x[128,8,64,64]", 64, (128, 64, 62, 62)),
+                                   (5, "conv3d 3->16 x[128,3,16,32,32]", 16, (128, 16, 14, 30, 30))):
+        inp = synth.host_inputs(wl)
+        a = (T(inp["x"]), T(inp["w"]), T(inp["b"]))
+        rm = torch.zeros(cout, device=dev)
+        rv = torch.ones(cout, device=dev)
+        out = torch.empty(oshape, device=dev)
+        f = lambda: nra.conv_bn_eval_forward(*a, rm, rv, out=out, eps=0.0)
+        times = {}
+        for mode in (["valu", "fp32", "default"] if wl == 4 else ["valu", "default"]):
+            if mode == "default":
+                os.environ.pop("NORMRED_CONV", None)
+            else:
+                os.environ["NORMRED_CONV"] = mode
+            time_calls(f, steps, warmup, torch, lambda: scrub.sum())
+            times[mode] = round(time_calls.last[len(time_calls.last) // 2], 4)
+            log("%s, producer %s: %.4f ms" % (name, mode, times[mode]))
+        os.environ.pop("NORMRED_CONV", None)
+        res["shapes"][name] = times
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,12 +350,17 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--conv-producers", action="store_true",
+                    help="time the conv producers alone (vector ALU against matrix cores) on the "
+                         "two model shapes, print one JSON line and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write the committed HBM traffic summary from two rocprofv3 "
                          "--pmc counter_collection.csv files of this script, then exit")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.conv_producers:
+        return conv_producers(args.steps, args.warmup)
     if args.gpus != 1:
         print("bench.py measures one GPU only: instance norm shards over the batch with no "
               "communication, and no multi-GPU path is built (--gpus %d refused)" % args.gpus,
