@@ -673,12 +673,10 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 // last tile starts earlier), none for a repeated tile
                 const int t = wave + 4 * i;
                 const int own = t < tiles ? 32 * t : BP;
-                float v0[16], v1[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    v0[r] = (acc0[r] + bias0) * pm0;
-                    v1[r] = (acc1[r] + bias1) * pm1;
-                }
+                // statistics of the raw sums; the bias and pre-multiplier enter once per
+                // workgroup (mean (m + b) * pm, M2 * pm^2) when the partial is written
+                const mf16& v0 = acc0;
+                const mf16& v1 = acc1;
                 if (ts == own) {  // the whole tile is owned (all but a box's last or repeated tiles)
                     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -764,10 +762,12 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         }
         __syncthreads();
         if (threadIdx.x < kC8Cout) {
-            Stat t = red[threadIdx.x];
+            const int ch = threadIdx.x;
+            Stat t = red[ch];
 #pragma unroll
-            for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + threadIdx.x]);
-            e.part[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = float4{t.n, t.mean, t.m2, 0.f};
+            for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + ch]);
+            const float bc = b ? b[ch] : 0.f, pc = e.pre_mul ? e.pre_mul[ch] : 1.f;
+            e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, (t.mean + bc) * pc, t.m2 * pc * pc, 0.f};
         }
     }
 }
