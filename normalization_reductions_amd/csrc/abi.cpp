@@ -585,7 +585,7 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         a.hi = d->clamp_hi;
         a.post_mul = d->post_mul;
         a.reduce_max_c = d->reduce_max_c;
-        e = launch_cl_apply(a, stream);
+        e = launch_cl_apply(a, L.cg, ws_at<float4>(workspace, L.partials), d->eps, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }

@@ -151,10 +151,14 @@ struct ClGeom {
 };
 ClGeom cl_geometry(int64_t N, int64_t C, int64_t SP, bool batch);
 size_t cl_partials_bytes(const ClGeom& g);  // float4 per (n, chunk, k)
+// Partials of every (n, chunk, k); for batch norm also their merge into stats (and the running
+// statistics). Instance norm leaves the merge to launch_cl_apply.
 hipError_t launch_cl_stats(const ClGeom& g, const float* c, const float* pre_mul, float4* partials,
                            float eps, GroupStat* stats, RunningStats run, hipStream_t stream);
 // ChainArgs as for the planar chain, with c and (without the max) out in [N, SP, C] layout.
-hipError_t launch_cl_apply(const ChainArgs& a, hipStream_t stream);
+// Batch norm reads a.stats; instance norm merges the partials of launch_cl_stats itself.
+hipError_t launch_cl_apply(const ChainArgs& a, const ClGeom& g, const float4* partials, float eps,
+                           hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // Utilities.

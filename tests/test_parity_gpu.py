@@ -664,6 +664,9 @@ CL_CASES = [
     ((1, 8, 3, 64), 64, True, False, True),
     ((2, 3, 6, 9, 11), 16, False, True, True),       # 3-D matrix-core ring, scalar staging
     ((3, 3, 5, 7, 8), 16, True, False, True),
+    ((2, 3, 5, 6, 7), 8, False, True, True),         # two lanes per position
+    ((3, 2, 9, 10), 4, False, False, True),          # one lane per position, in place
+    ((2, 2, 7, 9), 128, True, False, False),         # 32 lanes per position
 ]
 
 
