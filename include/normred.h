@@ -160,6 +160,10 @@ nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, in
  * statistics pass, then the conv again with the epilogue, so that c never goes to memory (the
  * workspace holds per-workgroup partial statistics, at most 4 MiB); with other pointers the
  * in-place plan above runs.
+ * Instance norm on the shapes C_in 3 -> C_out 16 (3-D, the IN3d page's model) and C_in 8 ->
+ * C_out 64 (2-D, other than the shape above), when the conv output is staged or channels last:
+ * the conv producer takes the statistics of its own output (the workspace holds N x J x C_out
+ * partials of 16 bytes, J a few per batch item), so no pass re-reads the conv output for them.
  * Precision: the conv is fp32-accurate. On that 2-D shape its products come from exact
  * three-part bf16 splits of x and w (six partial products; each part left out is below
  * 2^-24 |x w|), and the statistics of channels of at least 16384 values use four partial
@@ -169,8 +173,9 @@ nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, in
  * the max over channels contiguous): x is [N, (D,) H, W, C_in] and out is
  * [N, (D-2,) H-2, W-2, C_out], or [N, (D-2,) H-2, W-2] with reduce_max_c; w keeps its layout.
  * The arithmetic and the step order are the same. C_out <= 256 (else NR_ERR_UNSUPPORTED). The
- * statistics take a two-pass path over the conv output (staged in the workspace when
- * reduce_max_c, else written to `out` and normalized in place); no alignment is required.
+ * conv output is staged in the workspace when reduce_max_c, else written to `out` and normalized
+ * in place; the statistics come from the producer as above, or from a pass over it. No
+ * alignment is required.
  * ------------------------------------------------------------------------------------------ */
 #define NR_NORM_BATCH_TRAIN 1
 #define NR_NORM_INSTANCE 2

@@ -328,6 +328,7 @@ struct ChainLayout {
     int cfg_idx = -1, P = 0;
     size_t exch = 0, c8part = 0, c8stats = 0;
     size_t cbuf = 0, partials = 0, stats = 0, bytes = 0;
+    int64_t ring_J = 0;     // instance norm: slots of the ring producer's own statistics (0: none)
     SplitGeom sg;
     ClGeom cg;              // channels last
 };
@@ -341,10 +342,18 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
     ChainLayout L;
     size_t off = kHeaderBytes;
     const int64_t groups = batch ? g.Cout : g.N * g.Cout;
+    // instance norm on a ring producer shape: the producer takes the statistics of its output
+    // itself ([N][J][C_out] partials), so no pass re-reads the conv output for them
+    L.ring_J = batch ? 0 : ring_stats_slots(g);
     if (g.cl) {
         // channels last: conv output staged only for the max over channels (else written to
-        // `out` and normalized in place), partials per (n, chunk, k), group statistics
+        // `out` and normalized in place), partials per (n, chunk, k) or the ring producer's
+        // slots, group statistics
         L.cg = cl_geometry(g.N, g.Cout, g.SP, batch);
+        if (L.ring_J > 0) {
+            L.cg.chunk = 0;  // the slots stand in for the chunks
+            L.cg.chunks = L.ring_J;
+        }
         if (reduce_max_c) {
             L.cbuf = off;
             off = align_up(off + (size_t)(g.N * g.Cout * g.SP) * sizeof(float), kWsAlign);
@@ -378,9 +387,13 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
     }
     L.cbuf = off;
     off = align_up(off + (size_t)(g.N * g.Cout * g.SP) * sizeof(float), kWsAlign);
-    L.sg = split_geometry(g.N, g.Cout, g.SP, batch, g.SP % 4 == 0);
     L.partials = off;
-    off = align_up(off + (size_t)(L.sg.slices * L.sg.chunks) * sizeof(float2), kWsAlign);
+    if (L.ring_J > 0) {
+        off = align_up(off + (size_t)(g.N * L.ring_J * g.Cout) * sizeof(float4), kWsAlign);
+    } else {
+        L.sg = split_geometry(g.N, g.Cout, g.SP, batch, g.SP % 4 == 0);
+        off = align_up(off + (size_t)(L.sg.slices * L.sg.chunks) * sizeof(float2), kWsAlign);
+    }
     L.stats = off;
     off = align_up(off + (size_t)groups * sizeof(GroupStat), kWsAlign);
     L.bytes = off;
@@ -561,12 +574,18 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         if (L.cg.N * L.cg.chunks > 0x7fffffffLL || L.cg.chunks > 0x7fffffffLL)
             return fail(NR_ERR_UNSUPPORTED, "%s: too many statistics chunks for one launch", fn);
         float* c = d->reduce_max_c ? ws_at<float>(workspace, L.cbuf) : out;
-        hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
-        if (e != hipSuccess) return hip_fail(e, fn);
+        float4* part = ws_at<float4>(workspace, L.partials);
         GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
-        e = launch_cl_stats(L.cg, c, d->pre_mul, ws_at<float4>(workspace, L.partials), d->eps,
-                            stats, RunningStats{d->running_mean, d->running_var, d->momentum},
-                            stream);
+        hipError_t e;
+        if (L.ring_J > 0) {
+            e = launch_conv_k3_stats(g, x, w, b, c, RingStats{part, d->pre_mul, L.ring_J}, stream);
+        } else {
+            e = launch_conv_k3(g, x, w, b, c, stream);
+            if (e == hipSuccess)
+                e = launch_cl_stats(L.cg, c, d->pre_mul, part, d->eps, stats,
+                                    RunningStats{d->running_mean, d->running_var, d->momentum},
+                                    stream);
+        }
         if (e != hipSuccess) return hip_fail(e, fn);
         ChainArgs a;
         a.c = c;
@@ -585,7 +604,7 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         a.hi = d->clamp_hi;
         a.post_mul = d->post_mul;
         a.reduce_max_c = d->reduce_max_c;
-        e = launch_cl_apply(a, L.cg, ws_at<float4>(workspace, L.partials), d->eps, stream);
+        e = launch_cl_apply(a, L.cg, part, d->eps, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }
@@ -626,16 +645,24 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }
-    if (L.sg.slices * L.sg.chunks > 0x7fffffffLL)
+    if (L.ring_J > 0 ? g.N * g.Cout > 0x7fffffffLL : L.sg.slices * L.sg.chunks > 0x7fffffffLL)
         return fail(NR_ERR_UNSUPPORTED, "%s: too many statistics chunks for one launch", fn);
 
     float* c = ws_at<float>(workspace, L.cbuf);
-    float2* partials = ws_at<float2>(workspace, L.partials);
     GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
-    hipError_t e = launch_conv_k3(g, x, w, b, c, stream);
-    if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_split_stats(L.sg, c, d->pre_mul, partials, d->eps, stats, nullptr, nullptr,
-                           RunningStats{d->running_mean, d->running_var, d->momentum}, stream, true);
+    hipError_t e;
+    if (L.ring_J > 0) {
+        const RingStats rs{ws_at<float4>(workspace, L.partials), d->pre_mul, L.ring_J};
+        e = launch_conv_k3_stats(g, x, w, b, c, rs, stream);
+        if (e == hipSuccess) e = launch_ring_stats_merge(g, rs, d->eps, stats, stream);
+    } else {
+        e = launch_conv_k3(g, x, w, b, c, stream);
+        if (e == hipSuccess)
+            e = launch_split_stats(L.sg, c, d->pre_mul, ws_at<float2>(workspace, L.partials), d->eps,
+                                   stats, nullptr, nullptr,
+                                   RunningStats{d->running_mean, d->running_var, d->momentum},
+                                   stream, true);
+    }
     if (e != hipSuccess) return hip_fail(e, fn);
     ChainArgs a;
     a.c = c;

@@ -128,12 +128,231 @@ __global__ __launch_bounds__(kConvBlock) void conv_k3_kernel(ConvGeom g, const f
 typedef float mf4 __attribute__((ext_vector_type(4)));
 constexpr int kMfmaBlock = 256;  // 4 waves
 
-template <int DIMS, int KS, int WAVES_N, int MT, int PF, bool VEC, bool CL>
-__global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
+// Floats of the ring producer's LDS before its statistics area: the larger of the 4-slot input
+// ring and W plus the bias.
+__host__ __device__ inline int ring_main_floats(const ConvGeom& g, const ConvRing& rg, int dims)
+{
+    const int ring_f = 4 * (int)g.Cin * rg.inner_in;
+    const int w_f = (int)g.Cout * ((int)g.Cin * (dims == 3 ? 27 : 9) + 1);
+    return ring_f > w_f ? ring_f : w_f;
+}
+
+// The workgroup holding tile t when `total` tiles are cut into G equal contiguous ranges
+// [total * w / G, total * (w + 1) / G): the largest w with total * w / G <= t.
+__host__ __device__ inline int64_t ring_wg_of(int64_t t, int64_t total, int64_t G)
+{
+    return ((t + 1) * G - 1) / total;
+}
+
+// Chan's merge of a step's statistics b (b.n > 0) into a lane's running statistics a, with the
+// hardware reciprocal (1 ulp) for the weight: it runs once per tile step, inside the matrix
+// loop. The exact merge (chan_merge) combines lanes, waves and workgroups.
+__device__ __forceinline__ Stat merge_step(Stat a, Stat b)
+{
+    Stat r;
+    r.n = a.n + b.n;
+    const float f = b.n * __builtin_amdgcn_rcpf(r.n);
+    const float d = b.mean - a.mean;
+    r.mean = fmaf(d, f, a.mean);
+    r.m2 = a.m2 + b.m2 + d * d * a.n * f;
+    return r;
+}
+
+// Two-pass statistics of V values (all valid), summed as a tree.
+template <int V>
+__device__ __forceinline__ Stat tile_stat(const float* v)
+{
+    float t[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) t[i] = v[i];
+#pragma unroll
+    for (int w = 1; w < V; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < V; i += 2 * w) t[i] += t[i + w];
+    const float mean = t[0] * (1.f / V);
+#pragma unroll
+    for (int i = 0; i < V; ++i) t[i] = (v[i] - mean) * (v[i] - mean);
+#pragma unroll
+    for (int w = 1; w < V; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < V; i += 2 * w) t[i] += t[i + w];
+    return Stat{(float)V, mean, t[0]};
+}
+
+// Statistics of one tile step, from the lane's valid values. Planar: channel ch at positions
+// p0 .. p0 + 3 of each of the MT tiles; channels last: channels 4q + r at position
+// (t0 + mt) * 16 + r16. Steps whose tiles all lie inside the slice (the wave-uniform common
+// case) skip the masks.
+template <int MT, bool CL>
+__device__ __forceinline__ void ring_tile_stats(const mf4* acc, int t0, int thi, int shift,
+                                                int inner_out, int q, int r16, Stat* run, float* sh)
+{
+    const bool whole = t0 + MT <= thi && t0 * 16 - shift >= 0 && (t0 + MT) * 16 - shift <= inner_out;
+    if (CL) {
+        // channels last: MT values per channel and step, too few for a merge each; shifted sums
+        // instead (run[r] holds the shift K in .mean, the sums of (v - K) and (v - K)^2 in .m2
+        // and sh[r]), the shift being the lane's first step mean, so |mean - K| stays within a
+        // few standard deviations and the final M2 = S2 - S1^2 / n loses little
+        const bool first = run[0].n == 0.f;
+        if (whole) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) m += acc[mt][r];
+                const float K = first ? m * (1.f / MT) : run[r].mean;
+                float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float d = acc[mt][r] - K;
+                    s1 += d;
+                    s2 = fmaf(d, d, s2);
+                }
+                run[r].mean = K;
+                run[r].m2 += s2;
+                run[r].n += (float)MT;
+                sh[r] += s1;
+            }
+            return;
+        }
+        bool ok[MT];
+        int cnt = 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            ok[mt] = t0 + mt < thi && (t0 + mt) * 16 + r16 < inner_out;
+            cnt += ok[mt];
+        }
+        if (cnt == 0) return;
+        const float inv = __builtin_amdgcn_rcpf((float)cnt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float m = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) m += ok[mt] ? acc[mt][r] : 0.f;
+            const float K = first ? m * inv : run[r].mean;
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float d = ok[mt] ? acc[mt][r] - K : 0.f;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+            run[r].mean = K;
+            run[r].m2 += s2;
+            run[r].n += (float)cnt;
+            sh[r] += s1;
+        }
+        return;
+    }
+    // planar: 4 * MT values of channel ch per step, two-pass, merged into the running statistics
+    if (whole) {
+        float v[4 * MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[4 * mt + r] = acc[mt][r];
+        run[0] = merge_step(run[0], tile_stat<4 * MT>(v));
+        return;
+    }
+    bool ok[MT][4];
+    int cnt = 0;
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int p0 = (t0 + mt) * 16 + 4 * q - shift;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ok[mt][r] = t0 + mt < thi && p0 + r >= 0 && p0 + r < inner_out;
+            cnt += ok[mt][r];
+            s += ok[mt][r] ? acc[mt][r] : 0.f;
+        }
+    }
+    if (cnt == 0) return;
+    const float mean = s / (float)cnt;
+    float m2 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float d = ok[mt][r] ? acc[mt][r] - mean : 0.f;
+            m2 = fmaf(d, d, m2);
+        }
+    run[0] = merge_step(run[0], Stat{(float)cnt, mean, m2});
+}
+
+__device__ __forceinline__ Stat shfl_xor_stat(Stat s, int off)
+{
+    return Stat{__shfl_xor(s.n, off), __shfl_xor(s.mean, off), __shfl_xor(s.m2, off)};
+}
+
+// End of this workgroup's part of batch item n: the lanes of a wave holding the same channel
+// merge by a butterfly (lower lanes first), the waves of a channel tile in order of wm through
+// LDS, and one thread per channel writes slot j = blockIdx.x - first_wg(n) of (n, k). Every
+// thread of the workgroup calls it.
+template <int WAVES_M, bool CL>
+__device__ __forceinline__ void ring_stats_flush(const ConvGeom& g, const ConvRing& rg,
+                                                 const RingStats& rs, float* lds, int64_t n,
+                                                 int wm, int wn, int q, int r16, Stat* run)
+{
+    Stat* red = reinterpret_cast<Stat*>(lds);  // [WAVES_M][Cout]
+    const int lane = threadIdx.x & 63;
+    if (CL) {
+        // lanes 16q .. 16q + 15 hold channels 4q .. 4q + 3 at 16 positions
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const Stat o = shfl_xor_stat(run[r], off);
+                run[r] = (lane & off) ? chan_merge(o, run[r]) : chan_merge(run[r], o);
+            }
+        if (r16 == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wm * (int)g.Cout + wn * 16 + 4 * q + r] = run[r];
+        }
+    } else {
+        // lanes r16, r16 + 16, r16 + 32, r16 + 48 hold channel wn * 16 + r16
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            const Stat o = shfl_xor_stat(run[0], off);
+            run[0] = (lane & off) ? chan_merge(o, run[0]) : chan_merge(run[0], o);
+        }
+        if (q == 0) red[wm * (int)g.Cout + wn * 16 + r16] = run[0];
+    }
+    __syncthreads();
+    const int64_t tpn = (int64_t)rg.OO * rg.T;  // tiles per batch item
+    const int64_t total = g.N * tpn;
+    const int64_t first = ring_wg_of(n * tpn, total, gridDim.x);
+    const int64_t j = blockIdx.x - first;
+    const bool last = ring_wg_of((n + 1) * tpn - 1, total, gridDim.x) == (int64_t)blockIdx.x;
+    for (int k = threadIdx.x; k < (int)g.Cout; k += kMfmaBlock) {
+        Stat st = red[k];
+        for (int m = 1; m < WAVES_M; ++m) st = chan_merge(st, red[m * (int)g.Cout + k]);
+        const float pm = rs.pre_mul ? rs.pre_mul[k] : 1.f;
+        float4* slot = rs.part + (n * rs.J) * g.Cout + k;
+        slot[j * g.Cout] = make_float4(st.n, st.mean * pm, st.m2 * pm * pm, 0.f);
+        if (last)
+            for (int64_t jj = j + 1; jj < rs.J; ++jj) slot[jj * g.Cout] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+}
+
+// With STATS the producer also takes the instance-norm statistics of its output while the
+// tiles are in registers (IN3d page, its step list: statistics per (n, k) over the spatial
+// extent; two-pass over each tile's values, merged by Chan's rule), so no pass re-reads c for
+// them. Slot j of batch item n holds the part of n that workgroup first_wg(n) + j produced:
+// (count, mean, M2, 0) of pre_mul * c per channel; the workgroup holding n's last tile marks
+// the slots after its own empty, so a reader merges slots 0..J-1 of every item in order.
+//
+// The statistics cost registers: the variants taking them are held to 3 waves per SIMD (168
+// VGPRs), and run at 3 workgroups per CU.
+template <int DIMS, int KS, int WAVES_N, int MT, int PF, bool VEC, bool CL, bool STATS>
+__global__ __launch_bounds__(kMfmaBlock) __attribute__((amdgpu_waves_per_eu(STATS ? 3 : 1, STATS ? 3 : 8)))
+void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
                                                                    const float* __restrict__ x,
                                                                    const float* __restrict__ w,
                                                                    const float* __restrict__ b,
-                                                                   float* __restrict__ c)
+                                                                   float* __restrict__ c,
+                                                                   RingStats rs)
 {
     extern __shared__ float ring[];  // [4][Cin][inner_in], channels last: [4][inner_in][Cin]
     constexpr int KD = DIMS == 3 ? 3 : 1;
@@ -199,7 +418,10 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
     for (int i = (int)threadIdx.x; i < wcount; i += kMfmaBlock) ring[i] = w[i];
     for (int i = (int)threadIdx.x; i < (int)g.Cout; i += kMfmaBlock) ring[wcount + i] = b ? b[i] : 0.f;
     __syncthreads();
-    int tap[KS];
+    // The packed taps depend on q alone: a table [4][KS] in LDS after the ring (and the
+    // statistics area), read once per slice, keeps them out of the step loop's registers.
+    int* tapt = reinterpret_cast<int*>(ring + ring_main_floats(g, rg, DIMS) +
+                                       (STATS ? WAVES_M * (int)g.Cout * 3 : 0));
     float bw[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -216,7 +438,7 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
             in_off = rem % 3;
         }
         const int lds_off = CL ? in_off * Cin + ci : ci * rg.inner_in + in_off;
-        tap[s] = valid ? (a << 24) | lds_off : 0;
+        if (wave == 0 && r16 == 0) tapt[q * KS + s] = valid ? (a << 24) | lds_off : 0;
         bw[s] = valid ? ring[ch * K + k] : 0.f;
     }
     // accumulator start: the bias of the channel(s) a lane's 4 results belong to (planar: its
@@ -225,6 +447,15 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
 #pragma unroll
     for (int r = 0; r < 4; ++r) bias4[r] = ring[wcount + (CL ? wn * 16 + 4 * q + r : ch)];
     __syncthreads();
+    // running statistics of this lane's channel(s) over the current batch item: planar, channel
+    // ch; channels last, channels wn * 16 + 4q + r
+    Stat run[CL ? 4 : 1];
+    float sh[CL ? 4 : 1];  // channels last: sums of (v - shift), see ring_tile_stats
+#pragma unroll
+    for (int r = 0; r < (CL ? 4 : 1); ++r) {
+        run[r] = stat_empty();
+        sh[r] = 0.f;
+    }
 
     const int64_t total = (int64_t)g.N * rg.OO * rg.T;
     const int64_t begin = total * blockIdx.x / gridDim.x;
@@ -250,8 +481,10 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
         // slot offsets of this step's taps
         int koff[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            koff[s] = ((o + (tap[s] >> 24)) & 3) * slice_floats + (tap[s] & 0xFFFFFF);
+        for (int s = 0; s < KS; ++s) {
+            const int tt = tapt[q * KS + s];
+            koff[s] = ((o + (tt >> 24)) & 3) * slice_floats + (tt & 0xFFFFFF);
+        }
         const int shift = (!CL && rg.vec_out) ? (int)(((int64_t)o * rg.inner_out) & 3) : 0;
         float* cs = c + (n * g.Cout + ch) * g.SP + (int64_t)o * rg.inner_out;
 
@@ -272,17 +505,37 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
             mf4 acc[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = bias4;
+            // channels last: D = W x X, so a lane receives 4 consecutive channels of one
+            // position (D[m][n] lands in lane n + 16*(m/4), register m%4)
+            auto mfma = [&](int s, int mt, float av) {
+                acc[mt] = CL ? __builtin_amdgcn_mfma_f32_16x16x4f32(bw[s], av, acc[mt], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x4f32(av, bw[s], acc[mt], 0, 0, 0);
+            };
+            if (STATS) {
+                // the gathers of 4 taps issued ahead of their matrix instructions: left to itself
+                // the scheduler serializes each gather with its instruction in these variants
+                constexpr int kB = 4;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+                for (int s0 = 0; s0 < KS; s0 += kB) {
+                    float av[kB][MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const float av = ring[base[mt] + koff[s]];
-                    // channels last: D = W x X, so a lane receives 4 consecutive channels of
-                    // one position (D[m][n] lands in lane n + 16*(m/4), register m%4)
-                    acc[mt] = CL ? __builtin_amdgcn_mfma_f32_16x16x4f32(bw[s], av, acc[mt], 0, 0, 0)
-                                 : __builtin_amdgcn_mfma_f32_16x16x4f32(av, bw[s], acc[mt], 0, 0, 0);
+                    for (int i = 0; i < kB; ++i)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            if (s0 + i < KS) av[i][mt] = ring[base[mt] + koff[s0 + i]];
+#pragma unroll
+                    for (int i = 0; i < kB; ++i)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            if (s0 + i < KS) mfma(s0 + i, mt, av[i][mt]);
                 }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) mfma(s, mt, ring[base[mt] + koff[s]]);
             }
+            if (STATS) ring_tile_stats<MT, CL>(acc, t0, thi, shift, rg.inner_out, q, r16, run, sh);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if (t0 + mt >= thi) continue;
@@ -312,6 +565,25 @@ __global__ __launch_bounds__(kMfmaBlock) void conv_k3_ring_kernel(ConvGeom g, Co
         __syncthreads();
         cur = sl;
         t = (sl + 1) * rg.T;
+        if (STATS && (t >= end || o + 1 == rg.OO)) {  // this workgroup's part of item n is done
+            if (CL) {
+                // shifted sums to (count, mean, M2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float nn = run[r].n;
+                    const float s1 = sh[r];
+                    run[r] = nn > 0.f ? Stat{nn, run[r].mean + s1 / nn, fmaxf(run[r].m2 - s1 * s1 / nn, 0.f)}
+                                      : stat_empty();
+                }
+            }
+            ring_stats_flush<WAVES_M, CL>(g, rg, rs, ring + ring_main_floats(g, rg, DIMS), n, wm,
+                                          wn, q, r16, run);
+#pragma unroll
+            for (int r = 0; r < (CL ? 4 : 1); ++r) {
+                run[r] = stat_empty();
+                sh[r] = 0.f;
+            }
+        }
     }
 }
 
@@ -959,25 +1231,55 @@ int ring_grid(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu)
 
 template <int DIMS, int KS, int WAVES_N, int MT, int PF>
 hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, const float* x,
-                       const float* w, const float* b, float* c, hipStream_t stream)
+                       const float* w, const float* b, float* c, const RingStats* rs,
+                       hipStream_t stream)
 {
-    // the ring, which first holds W (C_out x K floats) and the bias while the lanes take theirs
-    const size_t lds = std::max<size_t>(4 * (size_t)g.Cin * rg.inner_in,
-                                        (size_t)g.Cout * (g.Cin * (DIMS == 3 ? 27 : 9) + 1)) * sizeof(float);
+    // the ring, which first holds W (C_out x K floats) and the bias while the lanes take theirs;
+    // with statistics, one Stat per (wave row, channel) after it; then the tap table
+    constexpr int WAVES_M = (kMfmaBlock / 64) / WAVES_N;
+    const size_t lds = (size_t)ring_main_floats(g, rg, DIMS) * sizeof(float) +
+                       (rs ? (size_t)WAVES_M * g.Cout * sizeof(Stat) : 0) + 4 * KS * sizeof(int);
     const int grid = ring_grid(g, rg, wgs_per_cu);
     const dim3 gd(grid), bd(kMfmaBlock);
-    if (g.cl) {
-        if (rg.vec_in)
-            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true, true><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+    const RingStats none{nullptr, nullptr, 0};
+#define NR_RING(VEC, CL, ST)                                                                     \
+    conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, VEC, CL, ST><<<gd, bd, lds, stream>>>(          \
+        g, rg, x, w, b, c, rs ? *rs : none)
+    if (rs) {
+        if (g.cl && rg.vec_in)
+            NR_RING(true, true, true);
+        else if (g.cl)
+            NR_RING(false, true, true);
+        else if (rg.vec_in)
+            NR_RING(true, false, true);
         else
-            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false, true><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+            NR_RING(false, false, true);
     } else {
-        if (rg.vec_in)
-            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, true, false><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+        if (g.cl && rg.vec_in)
+            NR_RING(true, true, false);
+        else if (g.cl)
+            NR_RING(false, true, false);
+        else if (rg.vec_in)
+            NR_RING(true, false, false);
         else
-            conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, false, false><<<gd, bd, lds, stream>>>(g, rg, x, w, b, c);
+            NR_RING(false, false, false);
     }
+#undef NR_RING
     return hipGetLastError();
+}
+
+// The shapes the ring producer is compiled for: 2-D C_in 8 -> C_out 64 and 3-D C_in 3 -> 16,
+// with int32 offsets into one batch item.
+enum RingShape { kRingNone, kRing2d, kRing3d };
+constexpr int kRingWgs2d = 4, kRingWgs3d = 3;  // workgroups per CU of the two ring producers
+constexpr int kRingWgsStats = 3;                // either, taking statistics
+RingShape ring_shape(const ConvGeom& g)
+{
+    const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+    if (!small || conv_valu_forced()) return kRingNone;
+    if (g.dims == 2 && g.Cin == 8 && g.Cout == 64) return kRing2d;
+    if (g.dims == 3 && g.Cin == 3 && g.Cout == 16) return kRing3d;
+    return kRingNone;
 }
 
 constexpr int kC8B = 4;  // output rows per box of the 2-D matrix producer (2 measured ~8 % slower)
@@ -1048,10 +1350,10 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
                     g, x, w, b, c, C8Chain{});
             return hipGetLastError();
         }
-        if (g.dims == 2 && g.Cin == 8 && g.Cout == 64 && make_ring(g, x, c, 1, &rg))
-            return launch_ring<2, 18, 4, 4, 1>(g, rg, 4, x, w, b, c, stream);
-        if (g.dims == 3 && g.Cin == 3 && g.Cout == 16 && make_ring(g, x, c, 3, &rg))
-            return launch_ring<3, 21, 1, 2, 3>(g, rg, 3, x, w, b, c, stream);
+        if (ring_shape(g) == kRing2d && make_ring(g, x, c, 1, &rg))
+            return launch_ring<2, 18, 4, 4, 1>(g, rg, kRingWgs2d, x, w, b, c, nullptr, stream);
+        if (ring_shape(g) == kRing3d && make_ring(g, x, c, 3, &rg))
+            return launch_ring<3, 21, 1, 2, 3>(g, rg, kRingWgs3d, x, w, b, c, nullptr, stream);
     }
     const dim3 grid((unsigned)((g.SP + kConvBlock - 1) / kConvBlock), (unsigned)g.N,
                     (unsigned)((g.Cout + kKB - 1) / kKB));
@@ -1091,6 +1393,77 @@ hipError_t launch_fold_bn_eval(const ConvGeom& g, const float* w, const float* b
     const int64_t K = g.Cin * (g.dims == 3 ? 27 : 9);
     fold_bn_eval_kernel<<<dim3((unsigned)g.Cout), dim3(256), 0, stream>>>(w, b, rm, rv, gamma, beta,
                                                                          eps, scale, K, wf, bf);
+    return hipGetLastError();
+}
+}  // namespace nr
+
+namespace nr {
+namespace {
+
+// Slots for one tile count per slice: at most floor((L - 2) / m) + 2 workgroups meet a run of
+// L >= 2 tiles when every workgroup range holds at least m tiles (the first and last meet it
+// with a tile each, the others lie inside it).
+int64_t ring_slots_for(const ConvGeom& g, const ConvRing& rg, int wgs)
+{
+    const int64_t L = (int64_t)rg.OO * rg.T;
+    const int64_t total = g.N * L;
+    const int64_t G = ring_grid(g, rg, wgs);
+    const int64_t m = total / G;  // >= 1: the grid never exceeds the tiles
+    return L < 2 ? 1 : (L - 2) / m + 2;
+}
+
+__global__ __launch_bounds__(256) void ring_stats_merge_kernel(RingStats rs, int64_t N, int64_t C,
+                                                               float eps, GroupStat* __restrict__ stats)
+{
+    const int64_t grp = (int64_t)blockIdx.x * 256 + threadIdx.x;  // n * C + k
+    if (grp >= N * C) return;
+    const int64_t n = grp / C, k = grp - n * C;
+    const float4* pp = rs.part + n * rs.J * C + k;
+    Stat st = stat_empty();
+    for (int64_t j = 0; j < rs.J; ++j) {
+        const float4 v = pp[j * C];
+        st = chan_merge(st, Stat{v.x, v.y, v.z});
+    }
+    stats[grp] = GroupStat{0.f, st.mean, rsqrtf(st.m2 / st.n + eps), 0.f};
+}
+}  // namespace
+
+int64_t ring_stats_slots(const ConvGeom& g)
+{
+    const RingShape shape = ring_shape(g);
+    // the 2-D 64-wide shape keeps its own producer (faster than the ring)
+    if (shape == kRingNone || g.N == 0 || conv2d_c8_shape(g)) return 0;
+    // the tile count per slice depends on the output's alignment (planar): take the most slots
+    // over the alignments a call may bring
+    alignas(16) static const float probe[4] = {0.f, 0.f, 0.f, 0.f};
+    const int PF = shape == kRing2d ? 1 : 3;
+    int64_t J = 0;
+    for (int mis = 0; mis < 4; ++mis) {
+        ConvRing rg;
+        if (!make_ring(g, probe, probe + mis, PF, &rg)) return 0;
+        J = std::max(J, ring_slots_for(g, rg, kRingWgsStats));
+    }
+    return J;
+}
+
+hipError_t launch_conv_k3_stats(const ConvGeom& g, const float* x, const float* w, const float* b,
+                                float* c, RingStats rs, hipStream_t stream)
+{
+    const RingShape shape = ring_shape(g);
+    ConvRing rg;
+    if (shape == kRing2d && make_ring(g, x, c, 1, &rg) && ring_slots_for(g, rg, kRingWgsStats) <= rs.J)
+        return launch_ring<2, 18, 4, 4, 1>(g, rg, kRingWgsStats, x, w, b, c, &rs, stream);
+    if (shape == kRing3d && make_ring(g, x, c, 3, &rg) && ring_slots_for(g, rg, kRingWgsStats) <= rs.J)
+        return launch_ring<3, 21, 1, 2, 3>(g, rg, kRingWgsStats, x, w, b, c, &rs, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_stats_merge(const ConvGeom& g, const RingStats& rs, float eps,
+                                   GroupStat* stats, hipStream_t stream)
+{
+    const int64_t groups = g.N * g.Cout;
+    ring_stats_merge_kernel<<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream>>>(
+        rs, g.N, g.Cout, eps, stats);
     return hipGetLastError();
 }
 }  // namespace nr

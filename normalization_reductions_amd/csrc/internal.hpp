@@ -25,13 +25,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // -> apply. Groups are slices (instance norm) or channels (batch norm).
 // ---------------------------------------------------------------------------------------------
 struct SplitGeom {
-    int64_t S;        // slice length
-    int64_t slices;   // N*C
-    int64_t C;        // channels (slice's channel = slice % C)
-    int64_t chunk;    // elements per chunk (multiple of 4 * block), last chunk may be shorter
-    int64_t chunks;   // ceil(S / chunk)
-    bool batch;       // true: group = channel over all n; false: group = slice
-    bool vec;         // 16-B path (aligned pointers and S % 4 == 0)
+    int64_t S = 0;        // slice length
+    int64_t slices = 0;   // N*C
+    int64_t C = 0;        // channels (slice's channel = slice % C)
+    int64_t chunk = 0;    // elements per chunk (multiple of 4 * block), last chunk may be shorter
+    int64_t chunks = 0;   // ceil(S / chunk)
+    bool batch = false;   // true: group = channel over all n; false: group = slice
+    bool vec = false;     // 16-B path (aligned pointers and S % 4 == 0)
 };
 
 struct GroupStat {    // per group, written by the merge step
@@ -84,6 +84,14 @@ struct ConvRing {
     int vec_out;    // 16-byte output stores (aligned groups of 4 positions)
 };
 
+// Instance-norm statistics the ring producer takes of its own output: per batch item n, J slots
+// of partials per channel, merged in slot order by the reader.
+struct RingStats {
+    float4* part;          // [N][J][Cout]: (count, mean, M2, 0) of pre_mul * c
+    const float* pre_mul;  // [Cout] or NULL
+    int64_t J;             // slots per batch item
+};
+
 // Epilogue and statistics arguments of the 2-D C_in 8 -> C_out 64 matrix producer when it runs
 // a batch-norm chain by recomputation (statistics pass, merge, apply pass).
 struct C8Chain {
@@ -115,6 +123,16 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
                                      float eps, RunningStats run, hipStream_t stream);
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream);
+// Slots per batch item of the ring producer's own statistics for this shape, for any pointer
+// alignment; 0 when the ring producer does not run the shape.
+int64_t ring_stats_slots(const ConvGeom& g);
+// The conv of launch_conv_k3 through the ring producer, which also writes the instance-norm
+// partials rs (rs.J == ring_stats_slots(g) > 0).
+hipError_t launch_conv_k3_stats(const ConvGeom& g, const float* x, const float* w, const float* b,
+                                float* c, RingStats rs, hipStream_t stream);
+// Group statistics per (n, k) from those partials (slot order), for the planar chain epilogue.
+hipError_t launch_ring_stats_merge(const ConvGeom& g, const RingStats& rs, float eps,
+                                   GroupStat* stats, hipStream_t stream);
 
 // Eval-mode batch norm folded into conv weights: wf [Cout][Cin*k^dims], bf [Cout].
 hipError_t launch_fold_bn_eval(const ConvGeom& g, const float* w, const float* b, const float* rm,

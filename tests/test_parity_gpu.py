@@ -554,6 +554,14 @@ CHAIN_CASES = [
     # instance statistics and the max over 16 channels on 2-D shapes: 1596 and 16384 positions
     ((3, 4, 40, 44), 16, False, True, True),
     ((2, 2, 130, 130), 16, False, True, False),
+    # instance statistics taken by the ring producer itself: without the max (90 positions),
+    # one tile per workgroup (an item over 2 workgroups), workgroups spanning many items, and
+    # the 2-D ring shape
+    ((2, 3, 5, 7, 8), 16, False, False, True),
+    ((64, 3, 4, 5, 6), 16, False, True, True),
+    ((1000, 3, 3, 4, 5), 16, False, True, False),
+    ((900, 3, 3, 6, 7), 16, False, False, True),
+    ((3, 8, 9, 30), 64, False, True, True),
 ]
 
 
@@ -580,6 +588,30 @@ def test_conv_chain_general(dev, nra, orc, shape, cout, batch, red, full):
                                  reduce_max_c=red)
     err = maxerr(H(out), ref)
     _log("chain %s Cout %d batch %s max_c %s: max_abs_err %.3e" % (shape, cout, batch, red, err))
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("cl", [False, True])
+@pytest.mark.parametrize("red", [False, True])
+def test_conv_chain_ring_statistics_offset_inputs(dev, nra, orc, cl, red):
+    """Instance statistics taken inside the 3-D ring producer on inputs with a large common
+    offset: the conv output's mean is ~20 standard deviations from zero, which a sum-of-squares
+    shortcut without a shift would not survive."""
+    g = np.random.Generator(np.random.PCG64(4242 + 2 * cl + red))
+    shape = (6, 3, 7, 12, 13)
+    x = (10.0 + 0.5 * g.standard_normal(shape)).astype(np.float32)
+    w = (g.standard_normal((16, 3, 3, 3, 3)) * 0.3).astype(np.float32)
+    b = g.standard_normal(16).astype(np.float32)
+    pm = g.uniform(0.5, 1.5, 16).astype(np.float32)
+    xin = _to_cl(x) if cl else x
+    out = nra.conv_norm_epilogue_forward(T(xin, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_INSTANCE,
+                                         pre_mul=T(pm, dev), clamp=(-3.0, 3.0), reduce_max_c=red,
+                                         channels_last=cl)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=False, pre_mul=pm, clamp=(-3.0, 3.0),
+                                 reduce_max_c=red)
+    got = H(out) if (red or not cl) else np.moveaxis(H(out), -1, 1)
+    err = maxerr(got, ref)
+    _log("ring statistics, offset inputs, cl %s max_c %s: max_abs_err %.3e" % (cl, red, err))
     assert err <= TOL
 
 
@@ -667,6 +699,8 @@ CL_CASES = [
     ((2, 3, 5, 6, 7), 8, False, True, True),         # two lanes per position
     ((3, 2, 9, 10), 4, False, False, True),          # one lane per position, in place
     ((2, 2, 7, 9), 128, True, False, False),         # 32 lanes per position
+    ((64, 3, 4, 5, 6), 16, False, True, True),       # ring statistics: one tile per workgroup
+    ((1000, 3, 3, 4, 5), 16, False, False, True),    # workgroups spanning many items, in place
 ]
 
 
