@@ -650,20 +650,7 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
 
     float* c = ws_at<float>(workspace, L.cbuf);
     GroupStat* stats = ws_at<GroupStat>(workspace, L.stats);
-    hipError_t e;
-    if (L.ring_J > 0) {
-        const RingStats rs{ws_at<float4>(workspace, L.partials), d->pre_mul, L.ring_J};
-        e = launch_conv_k3_stats(g, x, w, b, c, rs, stream);
-        if (e == hipSuccess) e = launch_ring_stats_merge(g, rs, d->eps, stats, stream);
-    } else {
-        e = launch_conv_k3(g, x, w, b, c, stream);
-        if (e == hipSuccess)
-            e = launch_split_stats(L.sg, c, d->pre_mul, ws_at<float2>(workspace, L.partials), d->eps,
-                                   stats, nullptr, nullptr,
-                                   RunningStats{d->running_mean, d->running_var, d->momentum},
-                                   stream, true);
-    }
-    if (e != hipSuccess) return hip_fail(e, fn);
+    const RingStats rs{ws_at<float4>(workspace, L.partials), d->pre_mul, L.ring_J};
     ChainArgs a;
     a.c = c;
     a.out = out;
@@ -681,6 +668,25 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
     a.hi = d->clamp_hi;
     a.post_mul = d->post_mul;
     a.reduce_max_c = d->reduce_max_c;
+    hipError_t e;
+    if (L.ring_J > 0) {
+        e = launch_conv_k3_stats(g, x, w, b, c, rs, stream);
+        if (e == hipSuccess && chain_apply_slots_ok(a)) {
+            // the epilogue merges the slots itself
+            e = launch_chain_apply_slots(a, rs, d->eps, stream);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            return NR_OK;
+        }
+        if (e == hipSuccess) e = launch_ring_stats_merge(g, rs, d->eps, stats, stream);
+    } else {
+        e = launch_conv_k3(g, x, w, b, c, stream);
+        if (e == hipSuccess)
+            e = launch_split_stats(L.sg, c, d->pre_mul, ws_at<float2>(workspace, L.partials), d->eps,
+                                   stats, nullptr, nullptr,
+                                   RunningStats{d->running_mean, d->running_var, d->momentum},
+                                   stream, true);
+    }
+    if (e != hipSuccess) return hip_fail(e, fn);
     e = launch_chain_apply(a, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return NR_OK;

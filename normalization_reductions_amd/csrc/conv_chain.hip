@@ -1146,6 +1146,70 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_vec_kernel(ChainArgs 
     if (a.reduce_max_c) st_stream(reinterpret_cast<f4*>(a.out + n * a.SP) + i4, m);
 }
 
+// chain_apply_vec_kernel for instance statistics held in the ring producer's slots: each
+// workgroup merges its batch item's slots itself (slot order, as ring_stats_merge_kernel), so
+// no merge launch runs. The values of the first kPre channels are loaded before the merge
+// (indexes clamped, so the loads are unconditional) and their latency overlaps it.
+__global__ __launch_bounds__(kChainBlock) void chain_apply_slots_kernel(ChainArgs a, RingStats rs,
+                                                                       float eps)
+{
+    constexpr int kPre = 8;
+    extern __shared__ float coef_raw[];  // [Cout][4]: pm, mean, A, B; then [Cout] post
+    float4* coef = reinterpret_cast<float4*>(coef_raw);
+    float* post = coef_raw + 4 * a.Cout;
+    const int64_t n = blockIdx.y;
+    const int64_t i4 = min((int64_t)blockIdx.x * kChainBlock + threadIdx.x, a.SP / 4 - 1);
+    const f4* cp = reinterpret_cast<const f4*>(a.c + n * a.Cout * a.SP) + i4;
+    const int64_t plane4 = a.SP / 4;
+    f4 v[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) v[k] = cp[min<int64_t>(k, a.Cout - 1) * plane4];
+    for (int k = threadIdx.x; k < (int)a.Cout; k += kChainBlock) {
+        const float4* pp = rs.part + n * rs.J * a.Cout + k;
+        Stat st = stat_empty();
+        for (int64_t j0 = 0; j0 < rs.J; j0 += 8) {
+            float4 sv[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) sv[b] = pp[min<int64_t>(j0 + b, rs.J - 1) * a.Cout];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                if (j0 + b < rs.J) st = chan_merge(st, Stat{sv[b].x, sv[b].y, sv[b].z});
+        }
+        const float rstd = rsqrtf(st.m2 / st.n + eps);
+        coef[k] = make_float4(a.pre_mul ? a.pre_mul[k] : 1.f, st.mean,
+                              rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale,
+                              (a.beta ? a.beta[k] : 0.f) * a.out_scale);
+        post[k] = a.post_mul ? a.post_mul[k] : 1.f;
+    }
+    __syncthreads();
+    if ((int64_t)blockIdx.x * kChainBlock + threadIdx.x >= a.SP / 4) return;
+    f4 m = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    auto one = [&](int k, f4 cv) {
+        const float4 q = coef[k];
+        f4 z = (cv * q.x - q.y) * q.z + q.w;
+        if (a.clamp) {
+            z.x = fminf(fmaxf(z.x, a.lo), a.hi);
+            z.y = fminf(fmaxf(z.y, a.lo), a.hi);
+            z.z = fminf(fmaxf(z.z, a.lo), a.hi);
+            z.w = fminf(fmaxf(z.w, a.lo), a.hi);
+        }
+        z *= post[k];
+        if (a.reduce_max_c) {
+            m.x = fmaxf(m.x, z.x);
+            m.y = fmaxf(m.y, z.y);
+            m.z = fmaxf(m.z, z.z);
+            m.w = fmaxf(m.w, z.w);
+        } else {
+            st_stream(reinterpret_cast<f4*>(a.out + (n * a.Cout + k) * a.SP) + i4, z);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (k < a.Cout) one(k, v[k]);
+    for (int k = kPre; k < (int)a.Cout; ++k) one(k, cp[k * plane4]);
+    if (a.reduce_max_c) st_stream(reinterpret_cast<f4*>(a.out + n * a.SP) + i4, m);
+}
+
 __global__ __launch_bounds__(kChainBlock) void chain_apply_kernel(ChainArgs a)
 {
     const int64_t i = (int64_t)blockIdx.x * kChainBlock + threadIdx.x;
@@ -1366,6 +1430,22 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
     else
         conv_k3_kernel<2, false><<<grid, dim3(kConvBlock), 0, stream>>>(g, x, w, b, c);
     return hipGetLastError();
+}
+
+hipError_t launch_chain_apply_slots(const ChainArgs& a, const RingStats& rs, float eps,
+                                   hipStream_t stream)
+{
+    const int64_t n4 = a.SP / 4;
+    const dim3 grid((unsigned)((n4 + kChainBlock - 1) / kChainBlock), (unsigned)a.N);
+    const size_t lds = (size_t)a.Cout * 5 * sizeof(float);
+    chain_apply_slots_kernel<<<grid, dim3(kChainBlock), lds, stream>>>(a, rs, eps);
+    return hipGetLastError();
+}
+
+bool chain_apply_slots_ok(const ChainArgs& a)
+{
+    return (a.SP & 3) == 0 && !a.batch &&
+           ((reinterpret_cast<uintptr_t>(a.c) | reinterpret_cast<uintptr_t>(a.out)) & 15) == 0;
 }
 
 hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream)

@@ -156,6 +156,11 @@ struct ChainArgs {
 };
 
 hipError_t launch_chain_apply(const ChainArgs& a, hipStream_t stream);
+// The same epilogue for instance norm with the statistics still in the ring producer's slots
+// (each workgroup merges its item's slots); needs chain_apply_slots_ok(a).
+bool chain_apply_slots_ok(const ChainArgs& a);
+hipError_t launch_chain_apply_slots(const ChainArgs& a, const RingStats& rs, float eps,
+                                   hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // Channels-last chain: c [N, SP, C] (C contiguous). A group is (n, k) (instance) or k (batch);
