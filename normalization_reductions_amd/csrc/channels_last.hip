@@ -181,11 +181,10 @@ __global__ __launch_bounds__(kWave) void cl_merge_kernel(ClGeom g, const float* 
     const int64_t n0 = g.batch ? 0 : grp / g.C;
     const int64_t members = g.batch ? g.N : 1;  // batch items merged into this group
     const int64_t total = members * g.chunks;
-    Stat st = stat_empty();
-    for (int64_t q = lane; q < total; q += kWave) {
+    Stat st = lane_strided_merge<kWave>(total, [&](int64_t q) {
         const float4 p = partials[((n0 + q / g.chunks) * g.chunks + q % g.chunks) * g.C + k];
-        st = chan_merge(st, Stat{p.x, p.y, p.z});
-    }
+        return Stat{p.x, p.y, p.z};
+    });
     st = wave_merge<kWave>(st);
     if (lane == 0) {
         const float pm = pre_mul ? pre_mul[k] : 1.f;

@@ -64,6 +64,30 @@ __device__ __forceinline__ Stat wave_merge(Stat s)
     return s;
 }
 
+// Lane-strided merge of `total` items: lane l merges items l, l + WIDTH, l + 2 WIDTH, ... in
+// that order. The loads of 8 items are issued together (indexes clamped, so the loads are
+// unconditional) before their merges: one cache round trip per 8 items instead of one per item.
+// load(q) returns the Stat of item q < total.
+template <int WIDTH, class Load>
+__device__ __forceinline__ Stat lane_strided_merge(int64_t total, Load load)
+{
+    constexpr int kB = 8;
+    const int64_t lane = threadIdx.x & (WIDTH - 1);
+    Stat st = stat_empty();
+    for (int64_t q0 = lane; q0 < total; q0 += (int64_t)kB * WIDTH) {
+        Stat v[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t q = q0 + (int64_t)b * WIDTH;
+            v[b] = load(q < total ? q : total - 1);
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+            if (q0 + (int64_t)b * WIDTH < total) st = chan_merge(st, v[b]);
+    }
+    return st;
+}
+
 // Plain-sum butterfly (all lanes end with the same fixed-order sum).
 template <int WIDTH>
 __device__ __forceinline__ float wave_sum(float v)

@@ -1053,11 +1053,10 @@ __global__ __launch_bounds__(kWave) void c8_stats_merge_kernel(const float4* __r
                                                                 RunningStats run)
 {
     const int ch = blockIdx.x;
-    Stat st = stat_empty();
-    for (int i = (int)threadIdx.x; i < G; i += kWave) {
+    Stat st = lane_strided_merge<kWave>(G, [&](int64_t i) {
         const float4 p = part[(int64_t)ch * G + i];
-        st = chan_merge(st, Stat{p.x, p.y, p.z});
-    }
+        return Stat{p.x, p.y, p.z};
+    });
     st = wave_merge<kWave>(st);
     if (threadIdx.x == 0) {
         const float rstd = rsqrtf(st.m2 / st.n + eps);

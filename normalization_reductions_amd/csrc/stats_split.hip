@@ -150,14 +150,13 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
     const int64_t members = g.batch ? g.slices / g.C : 1;
     const int64_t total = members * g.chunks;
 
-    Stat st = stat_empty();
-    for (int64_t q = lane; q < total; q += kWave) {
+    Stat st = lane_strided_merge<kWave>(total, [&](int64_t q) {
         const int64_t mem = q / g.chunks;
         const int64_t ch = q - mem * g.chunks;
         const int64_t slice = g.batch ? mem * g.C + grp : grp;
         const float2 p = partials[slice * g.chunks + ch];
-        st = chan_merge(st, Stat{(float)chunk_len(g, ch), p.x, p.y});
-    }
+        return Stat{(float)chunk_len(g, ch), p.x, p.y};
+    });
     st = wave_merge<kWave>(st);
     if (lane == 0) {
         const int64_t c = grp % g.C;
