@@ -280,11 +280,6 @@ struct ClStage {
     float pm, gm, bt, qm;
 };
 
-// Defaults of the optional per-channel parameters (1 for the multipliers, 0 for beta), read
-// through the same unconditional global load as a given parameter (never written; not const,
-// which would place them in the constant address space and turn the loads into flat ones).
-__device__ float kClOne = 1.f, kClZero = 0.f;
-
 template <bool INST>
 __device__ __forceinline__ ClStage cl_stage_issue(const ChainArgs& a, const ClSrc& src, int64_t n)
 {
@@ -292,17 +287,17 @@ __device__ __forceinline__ ClStage cl_stage_issue(const ChainArgs& a, const ClSr
     const int R = kClBlock / C;
     const int k = threadIdx.x / R, r = threadIdx.x % R;
     ClStage S;
-    S.pm = *(a.pre_mul ? a.pre_mul + k : &kClOne);
-    S.gm = *(a.gamma ? a.gamma + k : &kClOne);
-    S.bt = *(a.beta ? a.beta + k : &kClZero);
-    S.qm = *(a.post_mul ? a.post_mul + k : &kClOne);
+    S.pm = *(a.pre_mul ? a.pre_mul + k : &kParamOne);
+    S.gm = *(a.gamma ? a.gamma + k : &kParamOne);
+    S.bt = *(a.beta ? a.beta + k : &kParamZero);
+    S.qm = *(a.post_mul ? a.post_mul + k : &kParamOne);
     if (INST) {
         const float4* pp = src.partials + n * src.g.chunks * C + k;
-        S.extra = stat_empty();
-        for (int64_t q = r + R; q < src.g.chunks; q += R) {  // only when chunks > R
-            const float4 v = pp[q * C];
-            S.extra = chan_merge(S.extra, Stat{v.x, v.y, v.z});
-        }
+        // chunks r + R, r + 2R, ... (only when chunks > R), 8 loads at a time
+        S.extra = src.g.chunks > R ? lane_strided_merge_by(src.g.chunks - R, R, [&](int64_t q) {
+            const float4 v = pp[(q + R) * C];
+            return Stat{v.x, v.y, v.z};
+        }) : stat_empty();
         S.p0 = pp[min<int64_t>(r, src.g.chunks - 1) * C];  // chunks >= 1
         S.pivot = pp[0].w;
         S.mean_d = S.rstd = 0.f;

@@ -88,6 +88,35 @@ __device__ __forceinline__ Stat lane_strided_merge(int64_t total, Load load)
     return st;
 }
 
+// The same with a runtime stride R (a power of two) among R adjacent lanes: lane l merges
+// items l % R, l % R + R, ... in that order.
+template <class Load>
+__device__ __forceinline__ Stat lane_strided_merge_by(int64_t total, int R, Load load)
+{
+    constexpr int kB = 8;
+    const int64_t r = threadIdx.x & (R - 1);
+    Stat st = stat_empty();
+    for (int64_t q0 = r; q0 < total; q0 += (int64_t)kB * R) {
+        Stat v[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t q = q0 + (int64_t)b * R;
+            v[b] = load(q < total ? q : total - 1);
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+            if (q0 + (int64_t)b * R < total) st = chan_merge(st, v[b]);
+    }
+    return st;
+}
+
+// Defaults of optional per-channel parameters (1 for the multipliers, 0 for a shift), read
+// through the same unconditional global load as a given parameter: `*(p ? p + k : &kParamOne)`
+// (never written; not const, which would place them in the constant address space and turn
+// the loads into flat ones). A load under a branch is waited for at the branch's end, which
+// would also wait for every load issued before it.
+static __device__ float kParamOne = 1.f, kParamZero = 0.f;
+
 // Plain-sum butterfly (all lanes end with the same fixed-order sum).
 template <int WIDTH>
 __device__ __forceinline__ float wave_sum(float v)

@@ -1146,9 +1146,9 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_vec_kernel(ChainArgs 
 }
 
 // chain_apply_vec_kernel for instance statistics held in the ring producer's slots: each
-// workgroup merges its batch item's slots itself (slot order, as ring_stats_merge_kernel), so
-// no merge launch runs. The values of the first kPre channels are loaded before the merge
-// (indexes clamped, so the loads are unconditional) and their latency overlaps it.
+// workgroup merges its batch item's slots itself, so no merge launch runs. The values of the
+// first kPre channels are loaded before the merge (indexes clamped, so the loads are
+// unconditional) and their latency overlaps it.
 __global__ __launch_bounds__(kChainBlock) void chain_apply_slots_kernel(ChainArgs a, RingStats rs,
                                                                        float eps)
 {
@@ -1160,25 +1160,41 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_slots_kernel(ChainArg
     const int64_t i4 = min((int64_t)blockIdx.x * kChainBlock + threadIdx.x, a.SP / 4 - 1);
     const f4* cp = reinterpret_cast<const f4*>(a.c + n * a.Cout * a.SP) + i4;
     const int64_t plane4 = a.SP / 4;
+    // R = kChainBlock / Cout adjacent threads per channel (Cout a power of two, 4..256): slot
+    // lane r takes slots r, r + R, ... and a butterfly across the R lanes (lower lanes first)
+    // merges them, a fixed order. Its loads go out before the data loads (loads complete in
+    // order), so the merge waits for them alone.
+    const int R = kChainBlock / (int)a.Cout;
+    const int kc = threadIdx.x / R, r = threadIdx.x & (R - 1);
+    const float4* pp = rs.part + n * rs.J * a.Cout + kc;
+    const Stat extra = rs.J > R ? lane_strided_merge_by(rs.J - R, R, [&](int64_t j) {
+        const float4 sv = pp[(j + R) * a.Cout];
+        return Stat{sv.x, sv.y, sv.z};
+    }) : stat_empty();  // slots r + R, r + 2R, ...: only when J > R
+    const float4 p0 = pp[min<int64_t>(r, rs.J - 1) * a.Cout];
+    const float pm = *(a.pre_mul ? a.pre_mul + kc : &kParamOne);
+    const float gm = *(a.gamma ? a.gamma + kc : &kParamOne);
+    const float bt = *(a.beta ? a.beta + kc : &kParamZero);
+    const float qm = *(a.post_mul ? a.post_mul + kc : &kParamOne);
     f4 v[kPre];
 #pragma unroll
     for (int k = 0; k < kPre; ++k) v[k] = cp[min<int64_t>(k, a.Cout - 1) * plane4];
-    for (int k = threadIdx.x; k < (int)a.Cout; k += kChainBlock) {
-        const float4* pp = rs.part + n * rs.J * a.Cout + k;
-        Stat st = stat_empty();
-        for (int64_t j0 = 0; j0 < rs.J; j0 += 8) {
-            float4 sv[8];
-#pragma unroll
-            for (int b = 0; b < 8; ++b) sv[b] = pp[min<int64_t>(j0 + b, rs.J - 1) * a.Cout];
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                if (j0 + b < rs.J) st = chan_merge(st, Stat{sv[b].x, sv[b].y, sv[b].z});
+    {
+        Stat st = r < rs.J ? Stat{p0.x, p0.y, p0.z} : stat_empty();
+        st = chan_merge(st, extra);
+        const int lane = threadIdx.x & (kWave - 1);
+        for (int off = 1; off < R; off <<= 1) {
+            Stat o;
+            o.n = __shfl_xor(st.n, off);
+            o.mean = __shfl_xor(st.mean, off);
+            o.m2 = __shfl_xor(st.m2, off);
+            st = (lane & off) ? chan_merge(o, st) : chan_merge(st, o);
         }
-        const float rstd = rsqrtf(st.m2 / st.n + eps);
-        coef[k] = make_float4(a.pre_mul ? a.pre_mul[k] : 1.f, st.mean,
-                              rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale,
-                              (a.beta ? a.beta[k] : 0.f) * a.out_scale);
-        post[k] = a.post_mul ? a.post_mul[k] : 1.f;
+        if (r == 0) {
+            const float rstd = rsqrtf(st.m2 / st.n + eps);
+            coef[kc] = make_float4(pm, st.mean, rstd * gm * a.out_scale, bt * a.out_scale);
+            post[kc] = qm;
+        }
     }
     __syncthreads();
     if ((int64_t)blockIdx.x * kChainBlock + threadIdx.x >= a.SP / 4) return;
@@ -1336,6 +1352,7 @@ hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, co
 enum RingShape { kRingNone, kRing2d, kRing3d };
 constexpr int kRingWgs2d = 4, kRingWgs3d = 3;  // workgroups per CU of the two ring producers
 constexpr int kRingWgsStats = 3;                // either, taking statistics
+constexpr int64_t kRingMaxSlots = 128;          // statistics slots per batch item, at most
 RingShape ring_shape(const ConvGeom& g)
 {
     const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
@@ -1443,7 +1460,8 @@ hipError_t launch_chain_apply_slots(const ChainArgs& a, const RingStats& rs, flo
 
 bool chain_apply_slots_ok(const ChainArgs& a)
 {
-    return (a.SP & 3) == 0 && !a.batch &&
+    return (a.SP & 3) == 0 && !a.batch && a.Cout >= 4 && a.Cout <= kChainBlock &&
+           (a.Cout & (a.Cout - 1)) == 0 &&
            ((reinterpret_cast<uintptr_t>(a.c) | reinterpret_cast<uintptr_t>(a.out)) & 15) == 0;
 }
 
@@ -1522,7 +1540,9 @@ int64_t ring_stats_slots(const ConvGeom& g)
         if (!make_ring(g, probe, probe + mis, PF, &rg)) return 0;
         J = std::max(J, ring_slots_for(g, rg, kRingWgsStats));
     }
-    return J;
+    // small batches spread an item over many workgroups: past kRingMaxSlots slots the epilogue
+    // workgroups would spend longer merging them than a statistics pass over c takes
+    return J <= kRingMaxSlots ? J : 0;
 }
 
 hipError_t launch_conv_k3_stats(const ConvGeom& g, const float* x, const float* w, const float* b,

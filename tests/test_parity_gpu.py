@@ -562,6 +562,10 @@ CHAIN_CASES = [
     ((1000, 3, 3, 4, 5), 16, False, True, False),
     ((900, 3, 3, 6, 7), 16, False, False, True),
     ((3, 8, 9, 30), 64, False, True, True),
+    # 97 statistics slots per item (several per slot lane), and one item over 512 workgroups:
+    # past 128 slots the statistics come from a pass over the conv output instead
+    ((8, 3, 8, 34, 34), 16, False, True, True),
+    ((1, 3, 10, 34, 34), 16, False, True, True),
 ]
 
 
@@ -701,6 +705,8 @@ CL_CASES = [
     ((2, 2, 7, 9), 128, True, False, False),         # 32 lanes per position
     ((64, 3, 4, 5, 6), 16, False, True, True),       # ring statistics: one tile per workgroup
     ((1000, 3, 3, 4, 5), 16, False, False, True),    # workgroups spanning many items, in place
+    ((8, 3, 8, 34, 34), 16, False, True, True),      # 97 slots: several per chunk lane
+    ((1, 3, 10, 34, 34), 16, False, True, False),    # over 128 slots: statistics pass instead
 ]
 
 
