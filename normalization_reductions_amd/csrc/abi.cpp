@@ -371,7 +371,7 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
         // again with the chain epilogue (no conv output in HBM). The read-once plan's exchange
         // slots follow, for calls whose pointers the producer cannot take.
         L.recompute = true;
-        const int64_t G = std::min<int64_t>(g.N * ((g.OH + 3) / 4), kC8MaxGrid);
+        const int64_t G = conv2d_c8_grid_bound(g);
         L.c8part = off;
         off = align_up(off + (size_t)(g.Cout * G) * sizeof(float4), kWsAlign);
         L.c8stats = off;

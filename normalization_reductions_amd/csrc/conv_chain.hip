@@ -791,6 +791,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     constexpr int WSTAGE = 2 * kBfChunks * 3 * 64 * 8;  // bf16 of the staged B operands
     constexpr int ITEMS = ROWS * (W / 4) * 2;      // staging items: row x 4 columns x 4 channels
     static_assert(ITEMS <= 256, "one staging item per thread");
+    constexpr int TPW = ((B * OW + 31) / 32 + 3) / 4;  // tiles of 32 positions per wave and box
     __shared__ __attribute__((aligned(16))) unsigned short win[2 * WIN > WSTAGE ? 2 * WIN : WSTAGE];
     const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = l & 31, kk = l >> 5;
@@ -901,13 +902,13 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int BP = min(B, OH - o0) * OW;  // positions in this box: a multiple of 4, >= 62
         float* c0 = MODE == kC8Stats ? nullptr : c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
         float* c1 = MODE == kC8Stats ? nullptr : c0 + 32 * g.SP;
-        // exactly two tiles per wave, each 32 whole positions of the box: the last tile ends at
+        // exactly TPW tiles per wave, each 32 whole positions of the box: the last tile ends at
         // the box's last position (overlapping the one before), and waves with no tile left
         // repeat the last. Overlaps rewrite bitwise-identical values, and every lane issues the
-        // same 16 stores per box, so the wait for the next box's loads need not wait for them.
+        // same 8 TPW stores per box, so the wait for the next box's loads need not wait for them.
         const int tiles = (BP + 31) / 32;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TPW; ++i) {
             const int ts = min(32 * min(wave + 4 * i, tiles - 1), BP - 32);
             const int p = ts + m;
             const int r = p / OW;
@@ -1385,6 +1386,11 @@ bool conv2d_c8_shape(const ConvGeom& g)
 }
 
 int64_t conv2d_c8_stats_grid(const ConvGeom& g) { return c8_grid(g); }
+
+int64_t conv2d_c8_grid_bound(const ConvGeom& g)
+{
+    return std::min<int64_t>(g.N * ((g.OH + kC8B - 1) / kC8B), kC8MaxGrid);
+}
 
 bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out)
 {

@@ -112,6 +112,9 @@ bool conv2d_c8_shape(const ConvGeom& g);
 // Workgroups of its statistics pass (the number of partials per channel); at most kC8MaxGrid.
 constexpr int64_t kC8MaxGrid = 4096;
 int64_t conv2d_c8_stats_grid(const ConvGeom& g);
+// An upper bound of conv2d_c8_stats_grid on any device (one workgroup per box at most), for
+// sizing the partials before a device is known.
+int64_t conv2d_c8_grid_bound(const ConvGeom& g);
 // Whether a batch-norm chain of this shape and these pointers runs by recomputation (the
 // bf16x6 producer is not overridden for comparisons).
 bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out);
