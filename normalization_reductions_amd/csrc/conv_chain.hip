@@ -488,6 +488,11 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         const int shift = (!CL && rg.vec_out) ? (int)(((int64_t)o * rg.inner_out) & 3) : 0;
         float* cs = c + (n * g.Cout + ch) * g.SP + (int64_t)o * rg.inner_out;
 
+        // statistics of a step are taken one step late, between the next step's matrix
+        // instructions, whose latency then covers them (the vector ALU issues while the matrix
+        // unit runs); pt0 < 0: none pending
+        mf4 pacc[MT];
+        int pt0 = -1;
         for (int t0 = tlo + wm * MT; t0 < thi; t0 += WAVES_M * MT) {
             int base[MT];
 #pragma unroll
@@ -528,14 +533,18 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
                             if (s0 + i < KS) mfma(s0 + i, mt, av[i][mt]);
+                    if (s0 == kB && pt0 >= 0)
+                        ring_tile_stats<MT, CL>(pacc, pt0, thi, shift, rg.inner_out, q, r16, run, sh);
                 }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) pacc[mt] = acc[mt];
+                pt0 = t0;
             } else {
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) mfma(s, mt, ring[base[mt] + koff[s]]);
             }
-            if (STATS) ring_tile_stats<MT, CL>(acc, t0, thi, shift, rg.inner_out, q, r16, run, sh);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if (t0 + mt >= thi) continue;
@@ -561,6 +570,8 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
                 }
             }
         }
+        if (STATS && pt0 >= 0)  // the slice's last step
+            ring_tile_stats<MT, CL>(pacc, pt0, thi, shift, rg.inner_out, q, r16, run, sh);
         if (ahead) drop(o + 3);
         __syncthreads();
         cur = sl;
