@@ -231,6 +231,15 @@ def extras(torch, nra, x, y, steps, warmup):
     log("inorm x[16,64,256,256]: %.4f ms -> %.1f GB/s" % (per, b2 / (per / 1e3) / 1e9))
     del x2, y2
 
+    # standalone training batch norm on the batch-norm model's conv output shape (126 MB)
+    xb = torch.randn((128, 64, 62, 62), device=dev, generator=torch.Generator(device=dev).manual_seed(11))
+    yb = torch.empty_like(xb)
+    tot, per, med = time_calls(lambda: nra.bn_train_forward(xb, yb), steps, warmup, torch, flush)
+    bb = 2 * 4 * xb.numel()
+    out["bn_train_128x64x62x62"] = {"ms": round(per, 4), "GBps": round(bb / (per / 1e3) / 1e9, 1)}
+    log("bn_train x[128,64,62,62]: %.4f ms -> %.1f GB/s" % (per, bb / (per / 1e3) / 1e9))
+    del xb, yb
+
     i4 = synth.host_inputs(4)
     a4 = (T(i4["x"]), T(i4["w"]), T(i4["b"]))
     g4, be4 = T(i4["gamma"]), T(i4["beta"])
@@ -298,8 +307,8 @@ def extras(torch, nra, x, y, steps, warmup):
     out["conv2d_bn_eval_x2_128x8x64x64"] = {
         "ms": round(per, 4), "conv_TFLOPs": round(2 * 128 * 64 * 62 * 62 * 72 / (per / 1e3) / 1e12, 2)}
     log("conv2d+bn_eval(folded)+x2: %.4f ms" % per)
-    out["timing_note"] = ("workloads 2, 4, 5 and the eval conv: mean of HIP events around each "
-                          "call, a 512 MB buffer read before each call")
+    out["timing_note"] = ("workloads 2, 4, 5, the standalone batch norm and the eval conv: mean of "
+                          "HIP events around each call, a 512 MB buffer read before each call")
     return out
 
 
