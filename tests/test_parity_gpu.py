@@ -923,8 +923,10 @@ def test_conv_chain_max_c_misaligned_out(dev, nra, orc):
 def test_graph_capture_and_replay(dev, nra, orc):
     # every launch of these entry points can be captured: no hipMemsetAsync (fill kernels
     # instead), no synchronization, regular launches. Capture instance norm (read-once
-    # pipelined), batch norm and the IN3d conv chain once, then replay three times with eager
-    # changes of the inputs in between, checking every replay against the oracle.
+    # pipelined), batch norm and the IN3d conv chain once (4 items: statistics from a pass over
+    # the conv output; 32 items, planar and channels last: statistics taken by the producer),
+    # then replay three times with eager changes of the inputs in between, checking every
+    # replay against the oracle.
     import torch
 
     g = np.random.Generator(np.random.PCG64(5150))
@@ -935,8 +937,11 @@ def test_graph_capture_and_replay(dev, nra, orc):
     wc, bc, mc = T(i5["w"], dev), T(i5["b"], dev), T(i5["mult"], dev)
     yi, yb = torch.empty_like(xi), torch.empty_like(xb)
     yc = torch.empty((4, 14, 30, 30), device=dev)
+    xd = T(np.ascontiguousarray(i5["x"][:32]), dev)
+    xdl = torch.empty((32, 16, 32, 32, 3), device=dev)
+    yd, ydl = torch.empty((32, 14, 30, 30), device=dev), torch.empty((32, 14, 30, 30), device=dev)
     s = torch.cuda.Stream(device=dev)
-    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(3)]
+    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(5)]
     chain = dict(norm=nra.NR_NORM_INSTANCE, pre_mul=mc, clamp=(-1.0, 1.0), post_mul=mc,
                  reduce_max_c=True)
 
@@ -944,6 +949,9 @@ def test_graph_capture_and_replay(dev, nra, orc):
         nra.inorm_forward(xi, yi, workspace=ws[0], stream=s)
         nra.bn_train_forward(xb, yb, out_scale=2.0, workspace=ws[1], stream=s)
         nra.conv_norm_epilogue_forward(xc, wc, bc, yc, workspace=ws[2], stream=s, **chain)
+        nra.conv_norm_epilogue_forward(xd, wc, bc, yd, workspace=ws[3], stream=s, **chain)
+        nra.conv_norm_epilogue_forward(xdl, wc, bc, ydl, workspace=ws[4], stream=s,
+                                       channels_last=True, **chain)
 
     s.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(s):
@@ -958,6 +966,8 @@ def test_graph_capture_and_replay(dev, nra, orc):
             xi.mul_(1.5).add_(0.25)
             xb.mul_(0.5).sub_(1.0)
             xc.mul_(-1.0)
+            xd.mul_(-0.5).add_(0.125)
+            xdl.copy_(xd.permute(0, 2, 3, 4, 1))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -968,8 +978,11 @@ def test_graph_capture_and_replay(dev, nra, orc):
         e3 = maxerr(H(yc), orc.conv_norm_epilogue(H(xc), i5["w"], i5["b"], batch=False,
                                                   pre_mul=i5["mult"], clamp=(-1.0, 1.0),
                                                   post_mul=i5["mult"], reduce_max_c=True))
-        _log("graph replay %d: max_abs_err %.3e %.3e %.3e" % (rep, e1, e2, e3))
-        assert max(e1, e2, e3) <= TOL
+        rd = orc.conv_norm_epilogue(H(xd), i5["w"], i5["b"], batch=False, pre_mul=i5["mult"],
+                                    clamp=(-1.0, 1.0), post_mul=i5["mult"], reduce_max_c=True)
+        e4, e5 = maxerr(H(yd), rd), maxerr(H(ydl), rd)
+        _log("graph replay %d: max_abs_err %.3e %.3e %.3e %.3e %.3e" % (rep, e1, e2, e3, e4, e5))
+        assert max(e1, e2, e3, e4, e5) <= TOL
 
 
 def test_native_c_abi_roundtrip(dev, orc, tmp_path):
