@@ -747,6 +747,36 @@ def test_conv_chain_channels_last(dev, nra, orc, shape, cout, batch, red, full):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("red", [False, True])
+def test_conv_chain_channels_last_misaligned_out(dev, nra, orc, red):
+    # `out` four bytes off 16-byte alignment: without the max the conv writes it directly
+    # (scalar stores) and the epilogue normalizes it in place with one thread per position,
+    # merging the producer's statistics slots itself; with the max only the maxima move
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(909 + red))
+    shape = (2, 3, 6, 9, 11)
+    x = g.standard_normal(shape).astype(np.float32)
+    w = (g.standard_normal((16, 3, 3, 3, 3)) * 0.3).astype(np.float32)
+    b = g.standard_normal(16).astype(np.float32)
+    pm = g.standard_normal(16).astype(np.float32)
+    osh = (2, 4, 7, 9) if red else (2, 4, 7, 9, 16)
+    n = int(np.prod(osh))
+    buf = torch.empty(n + 1, dtype=torch.float32, device=dev)
+    out = buf[1:].view(osh)
+    assert out.data_ptr() % 16 != 0
+    nra.conv_norm_epilogue_forward(T(_to_cl(x), dev), T(w, dev), T(b, dev), out=out,
+                                   norm=nra.NR_NORM_INSTANCE, pre_mul=T(pm, dev),
+                                   clamp=(-1.0, 1.0), post_mul=T(pm, dev), reduce_max_c=red,
+                                   channels_last=True)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=False, pre_mul=pm, clamp=(-1.0, 1.0),
+                                 post_mul=pm, reduce_max_c=red)
+    got = H(out) if red else np.moveaxis(H(out), -1, 1)
+    err = maxerr(got, ref)
+    _log("channels-last chain, misaligned out, max_c %s: max_abs_err %.3e" % (red, err))
+    assert err <= TOL
+
+
 def test_conv_chain_channels_last_running_statistics(dev, nra, orc):
     g = np.random.Generator(np.random.PCG64(4242))
     x = g.standard_normal((4, 3, 6, 10, 12)).astype(np.float32)
