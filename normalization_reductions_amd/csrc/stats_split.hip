@@ -16,6 +16,13 @@
 //      (the page's split-slice scheme with a final fixed-order combine instead of float
 //      atomics) and writes pivot, mean - pivot and 1/sqrt(var + eps).
 //   3. apply: one workgroup per (slice, chunk) normalizes its chunk (second read of x).
+// Slices that do not start on 16-byte boundaries (S not a multiple of 4) in 16-byte aligned
+// tensors take flat variants of the partial and apply steps that keep 16-byte accesses: the
+// partial step gives each (slice, chunk) one wave, which reads the aligned 16-byte blocks
+// covering its range and masks the values outside it (reading a neighbour's edge values does
+// no harm); the apply step walks the whole tensor in aligned blocks, and each value takes the
+// coefficients of its own slice, so a block that straddles two slices is written whole and
+// right. Only the tensor's last block, when it is partial, uses 4-byte accesses.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -176,6 +183,130 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
     }
 }
 
+// Flat partial step: one wave per (slice, chunk) unit, kNW units per workgroup (unit u =
+// slice * chunks + chunk, as the partial index). x is 16-byte aligned; T = slices * S < 2^32.
+template <bool CACHED, bool FINAL>
+__global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g, const float* x,
+                                                                    const float* pre_mul,
+                                                                    float2* partials, float eps,
+                                                                    GroupStat* stats,
+                                                                    float* save_mean,
+                                                                    float* save_invstd, int64_t units)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t u = (int64_t)blockIdx.x * kNW + threadIdx.x / kWave;
+    if (u >= units) return;  // whole waves only: the rest of the workgroup has no barrier
+    const int64_t slice = u / g.chunks;
+    const int64_t ch = u - slice * g.chunks;
+    const int64_t c = slice % g.C;
+    const float m = pre_mul ? pre_mul[c] : 1.f;
+    const float K = x[pivot_slice(group_of(g, slice)) * g.S] * m;
+    const int64_t T = g.slices * g.S;
+    const int64_t start = slice * g.S + ch * g.chunk;
+    const int64_t end = start + chunk_len(g, ch);
+    const int64_t b_lo = start >> 2, b_hi = (end + 3) >> 2;  // aligned blocks covering the unit
+    const f4* xv = reinterpret_cast<const f4*>(x);
+    Stat st = stat_empty();
+    for (int64_t b0 = b_lo; b0 < b_hi; b0 += 4 * kWave) {
+        float d[16];
+        bool in[16];
+        int n = 0;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t b = b0 + j * kWave + lane;
+            f4 v = f4{0.f, 0.f, 0.f, 0.f};
+            if (b < b_hi) {
+                if (4 * b + 3 < T) {
+                    v = CACHED ? xv[b] : ld_stream(xv + b);
+                } else {  // the tensor's last, partial block
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * b + e < T) v[e] = CACHED ? x[4 * b + e] : ld_stream1(x + 4 * b + e);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = 4 * b + e;
+                const bool ok = b < b_hi && i >= start && i < end;
+                in[4 * j + e] = ok;
+                d[4 * j + e] = ok ? fmaf(v[e], m, -K) : 0.f;
+                n += ok;
+                sum += d[4 * j + e];
+            }
+        }
+        if (n > 0) {
+            const float fn = (float)n, mean = sum / fn;
+            float q = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (in[i]) q = fmaf(d[i] - mean, d[i] - mean, q);
+            st = chan_merge(st, Stat{fn, mean, q});
+        }
+    }
+    st = wave_merge<kWave>(st);
+    if (lane == 0) {
+        if (FINAL) {
+            const float rstd = rsqrtf(st.m2 / st.n + eps);
+            stats[slice] = GroupStat{K, st.mean, rstd, 0.f};
+            if (save_mean) save_mean[slice] = K + st.mean;
+            if (save_invstd) save_invstd[slice] = rstd;
+        } else {
+            partials[u] = make_float2(st.mean, st.m2);
+        }
+    }
+}
+
+// Flat apply step: thread -> one aligned 16-byte block of the whole tensor (dealt so that each
+// XCD streams a contiguous eighth, as split_apply_vec_kernel); each value takes its own
+// slice's coefficients. x and y are 16-byte aligned; T = slices * S < 2^32.
+__global__ __launch_bounds__(kBlock) void split_apply_flat_kernel(SplitGeom g, const float* x,
+                                                                  float* y, const GroupStat* stats,
+                                                                  const float* gamma,
+                                                                  const float* beta,
+                                                                  float out_scale, int64_t nblocks)
+{
+    int64_t w = blockIdx.x;
+    const int64_t wgs = gridDim.x, w8 = wgs / 8 * 8;
+    if (w < w8) w = (w % 8) * (w8 / 8) + w / 8;
+    const int64_t b = w * kBlock + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint32_t T = (uint32_t)(g.slices * g.S), S = (uint32_t)g.S;
+    const uint32_t e0 = (uint32_t)(4 * b);
+    const bool whole = e0 + 3 < T;
+    f4 v = f4{0.f, 0.f, 0.f, 0.f};
+    if (whole) {
+        v = ld_stream(reinterpret_cast<const f4*>(x) + b);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e0 + e < T) v[e] = ld_stream1(x + e0 + e);
+    }
+    uint32_t sl = e0 / S, r = e0 - sl * S;  // slice and offset of the block's first value
+    f4 z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        while (r >= S) {  // at most 3 steps: the block holds 4 values
+            r -= S;
+            ++sl;
+        }
+        const int64_t slice = sl < (uint32_t)g.slices ? sl : g.slices - 1;  // tail past T
+        const int64_t c = slice % g.C;
+        const GroupStat st = stats[group_of(g, slice)];
+        const float A = st.rstd * (gamma ? gamma[c] : 1.f) * out_scale;
+        const float B = (beta ? beta[c] : 0.f) * out_scale;
+        z[e] = ((v[e] - st.pivot) - st.mean_d) * A + B;
+        ++r;
+    }
+    if (whole) {
+        st_stream(reinterpret_cast<f4*>(y) + b, z);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e0 + e < T) st_stream1(y + e0 + e, z[e]);
+    }
+}
+
 // Normalize pass, 16-byte path: one 1024-value sub-chunk of one slice per workgroup (one
 // vector per thread), a one-shot grid dealt so that each XCD streams a contiguous eighth of
 // the sub-chunks -- the fastest streaming pattern measured on MI355X.
@@ -247,11 +378,29 @@ SplitGeom split_geometry(int64_t N, int64_t C, int64_t S, bool batch, bool vec)
 }
 
 namespace {
+// The flat variants: slices off 16-byte boundaries in a 16-byte aligned tensor whose element
+// count fits the apply step's 32-bit indexing.
+bool split_flat(const SplitGeom& g, const void* x, const void* y)
+{
+    const int64_t T = g.slices * g.S;
+    return !g.vec && T > 0 && T <= 0xFFFFFFF0LL && (uintptr_t)x % 16 == 0 &&
+           (y == nullptr || (uintptr_t)y % 16 == 0);
+}
+
 template <bool FINAL>
 void launch_partial(const SplitGeom& g, const float* x, const float* pre_mul, float2* partials,
                     float eps, GroupStat* stats, float* save_mean, float* save_invstd,
                     hipStream_t stream, bool cached)
 {
+    if (split_flat(g, x, nullptr)) {
+        const int64_t units = g.slices * g.chunks;
+        const dim3 gd((unsigned)((units + kNW - 1) / kNW)), bd(kBlock);
+        if (cached)
+            split_partial_flat_kernel<true, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);
+        else
+            split_partial_flat_kernel<false, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);
+        return;
+    }
     const int64_t grid = g.slices * g.chunks;
     const dim3 gd((unsigned)grid), bd(kBlock);
     if (g.vec && cached)
@@ -294,6 +443,12 @@ hipError_t launch_split_apply(const SplitGeom& g, const float* x, float* y,
                               const GroupStat* stats, const float* gamma, const float* beta,
                               float out_scale, hipStream_t stream)
 {
+    if (split_flat(g, x, y)) {
+        const int64_t nblocks = (g.slices * g.S + 3) / 4;
+        split_apply_flat_kernel<<<dim3((unsigned)((nblocks + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream>>>(
+            g, x, y, stats, gamma, beta, out_scale, nblocks);
+        return hipGetLastError();
+    }
     const int64_t subs = (g.S + 4 * kBlock - 1) / (4 * kBlock);
     const int64_t total = g.slices * subs;
     if (g.vec && total <= 0x7fffffffLL) {

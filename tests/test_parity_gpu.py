@@ -190,7 +190,10 @@ def test_inorm_resident_configurations(dev, nra, orc, monkeypatch, block, vec, S
 
 
 EDGE_SHAPES = [(1, 1, 1), (3, 2, 5), (2, 3, 1023), (1, 1, 4), (2, 2, 65540), (1, 3, 262148),
-               (4, 2, 100000), (1, 1, 1048576), (2, 1, 1048580), (5, 7, 12600), (1, 1, 7)]
+               (4, 2, 100000), (1, 1, 1048576), (2, 1, 1048580), (5, 7, 12600), (1, 1, 7),
+               # S % 4 != 0 in aligned tensors (flat 16-byte path): several chunks per slice,
+               # and many one-chunk slices
+               (2, 3, 70001), (256, 64, 961)]
 
 
 @pytest.fixture(scope="module")
@@ -383,6 +386,22 @@ def test_inorm_affine_inplace_stats(dev, nra, orc, S):
     np.testing.assert_allclose(H(si), 1.0 / np.sqrt(var.ravel() + 1e-5), rtol=1e-5)
 
 
+@pytest.mark.parametrize("shape", [(3, 5, 961), (2, 2, 70003), (7, 3, 2)])
+def test_odd_slices_in_place(dev, nra, orc, shape):
+    # S % 4 != 0, y == x: the flat apply step reads and writes each 16-byte block in one thread,
+    # and the statistics pass finished reading before it
+    g = np.random.Generator(np.random.PCG64(shape[2] * 3 + shape[0]))
+    x = (g.standard_normal(shape) * 2.0 + 3.0).astype(np.float32)
+    xt = T(x, dev)
+    yt = nra.inorm_forward(xt, xt)
+    err_i = maxerr(H(yt), orc.instance_norm(x))
+    xt = T(x, dev)
+    yt = nra.bn_train_forward(xt, xt, out_scale=1.5)
+    err_b = maxerr(H(yt), orc.batch_norm_train(x, scale=1.5))
+    _log("odd slices in place %s: inorm %.3e, bn %.3e" % (shape, err_i, err_b))
+    assert max(err_i, err_b) <= TOL
+
+
 def test_inorm_unaligned_and_side_stream(dev, nra, orc):
     import torch
 
@@ -411,6 +430,7 @@ BN_SHAPES = [
     (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
     (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
     (65, 2, 32768),    # 2.1M values per channel: beyond the read-once index range -> split
+    (9, 5, 20003), (256, 64, 961),      # S % 4 != 0, flat 16-byte split path: several chunks
 ]
 
 
@@ -456,7 +476,8 @@ def test_bn_train_large_offset_small_spread(dev, nra, orc, shape):
 
 # running statistics: resident single-workgroup, pipelined, split (S % 4 != 0) and the
 # beyond-index-range split path; two steps in a row so the update compounds
-BN_RUNNING_SHAPES = [(128, 64, 3844), (5, 2, 7), (2, 4, 4100), (33, 2, 16000), (65, 2, 32768)]
+BN_RUNNING_SHAPES = [(128, 64, 3844), (5, 2, 7), (2, 4, 4100), (33, 2, 16000), (65, 2, 32768),
+                     (9, 5, 20003)]
 
 
 def _check_running(rm_gpu, rv_gpu, rm_ref, rv_ref, what):
