@@ -83,12 +83,14 @@ nr_status inorm_forward(const float* x, float* y, int64_t N, int64_t C, int64_t 
 /* Kernel variants for inorm_forward_ex (benchmarks and tests; inorm_forward = AUTO). */
 #define NR_VARIANT_AUTO 0     /* the library's choice for the shape */
 #define NR_VARIANT_RESIDENT 1 /* read-once: each slice held in registers, split over 1..32
-                                 concurrent workgroups that exchange partial statistics */
+                                 concurrent workgroups that exchange partial statistics; a
+                                 slice with S % 4 != 0 (S <= 65,530) is held by one
+                                 workgroup. Needs 16-byte aligned x and y */
 #define NR_VARIANT_SPLIT 2    /* streaming two-pass: partial statistics per chunk, a fixed-order
                                  merge, then a normalize pass (reads x twice) */
 
 /* As inorm_forward, with an explicit variant. A variant that cannot run this shape (e.g.
- * RESIDENT with a slice beyond 16 parts, or unaligned data) returns NR_ERR_UNSUPPORTED. */
+ * RESIDENT with a slice beyond 32 parts, or unaligned data) returns NR_ERR_UNSUPPORTED. */
 nr_status inorm_forward_ex(const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps,
                            const float* gamma, const float* beta, float* save_mean,
                            float* save_invstd, void* workspace, size_t workspace_bytes,

@@ -449,17 +449,27 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
 
     int cfg_idx = -1, P = 0;
     const bool res_ok = vec && choose_resident(S, false, false, &cfg_idx, &P) && (P == 1 || L.exchange);
+    // slices off 16-byte boundaries: one workgroup per slice (flat_norm.hip)
+    const bool flat_ok = S % 4 != 0 && aligned(x, 16) && aligned(y, 16) &&
+                         S <= flat_norm_max_len() && N * C <= 0x7fffffffLL;
     bool use_res = false;
     if (variant == NR_VARIANT_RESIDENT) {
-        if (!res_ok)
+        if (!res_ok && !flat_ok)
             return fail(NR_ERR_UNSUPPORTED,
-                        "%s: the resident variant needs 16-byte aligned x/y, S %% 4 == 0 and "
-                        "S <= %d (S=%lld)", fn, kMaxParts * 32768, (long long)S);
+                        "%s: the resident variant needs 16-byte aligned x/y and either S %% 4 == 0 "
+                        "with S <= %d, or S <= %lld (S=%lld)", fn, kMaxParts * 32768,
+                        (long long)flat_norm_max_len(), (long long)S);
         use_res = true;
     } else if (variant == NR_VARIANT_AUTO) {
-        use_res = res_ok;
+        use_res = res_ok || flat_ok;  // flat: faster than the split path from S = 7 up
     }
 
+    if (use_res && !res_ok) {
+        const hipError_t e = launch_flat_norm(x, y, N * C, C, S, eps, gamma, beta, save_mean,
+                                              save_invstd, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     if (use_res) {
         if (N * C * P > 0xF0000000LL || N * C > 0x7fffffffLL)  // counter headroom, grid limit
             return fail(NR_ERR_UNSUPPORTED, "%s: too many slices for the resident variant", fn);

@@ -1,0 +1,172 @@
+// flat_norm.hip -- read-once instance normalization for slices whose length is not a multiple
+// of 4, in a 16-byte aligned tensor: apart from the first, such slices start off 16-byte
+// boundaries, so the read-once kernels of resident_norm.hip (16-byte accesses from each slice's
+// start) do not apply.
+//
+// IN2d page, statement of the op (and the IN3d page's InstanceNorm3d reading): per (n, c) slice
+// of S values, mean and biased variance over the slice, y = (x - mean) / sqrt(var + eps), then
+// y * gamma[c] + beta[c] when the affine parameters are given.
+//
+// One workgroup per slice. Of the aligned 16-byte blocks of the whole tensor that the slice
+// [s*S, s*S + S) touches, those wholly inside it are spread over the threads (thread t holds
+// whole blocks t, t + BLOCK, ... in registers) and read and written with 16-byte accesses; the
+// slice's values in the partly covered first and last block (at most 3 each) are held by
+// threads 0 and 1 and read and written with 4-byte accesses. No value outside the slice is
+// touched, so every value of x is read once and every value of y written once, and in place
+// (y == x) the workgroups work on disjoint values.
+//
+// Statistics as in the other kernels: values shifted by the slice's first value (the pivot),
+// a two-pass (mean, M2) per thread over its registers, then pairwise (Chan) merges across the
+// wave (fixed butterfly) and across the waves (wave 0, fixed order): deterministic.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace nr {
+namespace {
+
+template <int BLOCK, int VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(BLOCK, BLOCK))) void
+flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, const float* gamma,
+                 const float* beta, float* save_mean, float* save_invstd)
+{
+    constexpr int NW = BLOCK / kWave;
+    __shared__ Stat wstat[NW];
+    __shared__ float coef[2];
+    const int tid = threadIdx.x;
+    const int64_t s = blockIdx.x;
+    const int64_t start = s * S;
+    const int len = (int)S;
+    const int off0 = (int)(start & 3);       // the slice's first value inside its first block
+    const int kw0 = off0 > 0 ? 1 : 0;        // first whole block (counted from the first block)
+    const int kw1 = (off0 + len) >> 2;       // one past the last whole block
+    const int nwb = kw1 > kw0 ? kw1 - kw0 : 0;
+    // head: the slice's values in a partly covered first block; tail: those in a partly
+    // covered last block that is not also the first
+    const int nh = off0 > 0 ? min(4, off0 + len) - off0 : 0;
+    const int nt = kw1 >= kw0 ? off0 + len - 4 * kw1 : 0;
+    const float K = x[start];
+
+    const int64_t wb0 = ((start - off0) >> 2) + kw0;  // tensor block index of whole block 0
+    const f4* xw = reinterpret_cast<const f4*>(x) + wb0;
+    f4 v[VEC];
+    if (nwb > 0) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[j] = ld_stream(xw + min(j * BLOCK + tid, nwb - 1));
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[j] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    int ne = 0;
+    int64_t eo = start;  // first edge value of this thread
+    if (tid == 0) {
+        ne = nh;
+    } else if (tid == 1) {
+        ne = nt;
+        eo = start + len - nt;
+    }
+    float ev[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        if (q < ne) ev[q] = ld_stream1(x + eo + q);
+
+    // Pivot-shifted values; registers past the last whole block become 0 and stay out of the
+    // count.
+    int cw = 0;
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const bool in = j * BLOCK + tid < nwb;
+        v[j] = in ? v[j] - K : f4{0.f, 0.f, 0.f, 0.f};
+        cw += in;
+        acc += v[j];
+    }
+    float sum = (acc.x + acc.y) + (acc.z + acc.w);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        ev[q] = q < ne ? ev[q] - K : 0.f;
+        sum += ev[q];
+    }
+    const int cnt = 4 * cw + ne;
+    const float fn = (float)cnt;
+    const float m = cnt > 0 ? sum / fn : 0.f;
+    f4 qa = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const f4 d = v[j] - m;
+        qa = j * BLOCK + tid < nwb ? qa + d * d : qa;
+    }
+    float q2 = (qa.x + qa.y) + (qa.z + qa.w);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const float d = ev[q] - m;
+        q2 = q < ne ? fmaf(d, d, q2) : q2;
+    }
+    Stat st = wave_merge<kWave>(Stat{fn, m, q2});
+    if (lane_id() == 0) wstat[tid / kWave] = st;
+    __syncthreads();
+    if (tid < kWave) {
+        Stat w = lane_id() < NW ? wstat[lane_id()] : stat_empty();
+        w = wave_merge<NW>(w);
+        if (tid == 0) {
+            const float rstd = rsqrtf(w.m2 / w.n + eps);
+            const int64_t c = s % C;
+            const float gm = gamma ? gamma[c] : 1.f;
+            const float bt = beta ? beta[c] : 0.f;
+            const float sc = rstd * gm;
+            coef[0] = sc;
+            coef[1] = fmaf(-w.mean, sc, bt);
+            if (save_mean) save_mean[s] = K + w.mean;
+            if (save_invstd) save_invstd[s] = rstd;
+        }
+    }
+    __syncthreads();
+    const float sc = coef[0], sh = coef[1];
+    f4* yw = reinterpret_cast<f4*>(y) + wb0;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int i = j * BLOCK + tid;
+        if (i < nwb) st_stream(yw + i, v[j] * sc + sh);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        if (q < ne) st_stream1(y + eo + q, fmaf(ev[q], sc, sh));
+}
+
+struct FlatCfg {
+    int block, vec;
+};
+// Ascending capacity; a slice of S values spans at most (S + 6) / 4 blocks.
+constexpr FlatCfg kFlatCfgs[] = {{64, 1}, {64, 4}, {256, 4}, {256, 16}, {512, 16}, {1024, 16}};
+
+}  // namespace
+
+int64_t flat_norm_max_len() { return 4 * 1024 * 16 - 6; }
+
+hipError_t launch_flat_norm(const float* x, float* y, int64_t slices, int64_t C, int64_t S,
+                            float eps, const float* gamma, const float* beta, float* save_mean,
+                            float* save_invstd, hipStream_t stream)
+{
+    if (S < 1 || S > flat_norm_max_len() || slices < 1 || slices > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    const int64_t need = (S + 6) / 4;
+    for (const FlatCfg& c : kFlatCfgs) {
+        if ((int64_t)c.block * c.vec < need) continue;
+        const dim3 grid((unsigned)slices), blk(c.block);
+#define NR_FLAT(B, V)                                                                             \
+    if (c.block == B && c.vec == V) {                                                             \
+        flat_norm_kernel<B, V><<<grid, blk, 0, stream>>>(x, y, C, S, eps, gamma, beta, save_mean, \
+                                                         save_invstd);                            \
+        return hipGetLastError();                                                                 \
+    }
+        NR_FLAT(64, 1)
+        NR_FLAT(64, 4)
+        NR_FLAT(256, 4)
+        NR_FLAT(256, 16)
+        NR_FLAT(512, 16)
+        NR_FLAT(1024, 16)
+#undef NR_FLAT
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nr

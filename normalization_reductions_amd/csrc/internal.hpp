@@ -20,6 +20,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Read-once normalization: see resident.hpp.
 
+// Read-once instance normalization of slices with S % 4 != 0 (flat_norm.hip): one workgroup
+// per slice, x and y 16-byte aligned, S <= flat_norm_max_len(), slices <= 2^31 - 1.
+int64_t flat_norm_max_len();
+hipError_t launch_flat_norm(const float* x, float* y, int64_t slices, int64_t C, int64_t S,
+                            float eps, const float* gamma, const float* beta, float* save_mean,
+                            float* save_invstd, hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------------
 // Streaming split path: partial statistics per (slice, chunk) -> fixed-order merge per group
 // -> apply. Groups are slices (instance norm) or channels (batch norm).

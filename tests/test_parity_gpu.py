@@ -388,8 +388,9 @@ def test_inorm_affine_inplace_stats(dev, nra, orc, S):
 
 @pytest.mark.parametrize("shape", [(3, 5, 961), (2, 2, 70003), (7, 3, 2)])
 def test_odd_slices_in_place(dev, nra, orc, shape):
-    # S % 4 != 0, y == x: the flat apply step reads and writes each 16-byte block in one thread,
-    # and the statistics pass finished reading before it
+    # S % 4 != 0, y == x. Instance norm: one workgroup per slice touching only its own values
+    # (S <= 65,530), else the split path; batch norm: the split path, whose flat apply step
+    # reads and writes each 16-byte block in one thread after the statistics pass has read x
     g = np.random.Generator(np.random.PCG64(shape[2] * 3 + shape[0]))
     x = (g.standard_normal(shape) * 2.0 + 3.0).astype(np.float32)
     xt = T(x, dev)
@@ -400,6 +401,44 @@ def test_odd_slices_in_place(dev, nra, orc, shape):
     err_b = maxerr(H(yt), orc.batch_norm_train(x, scale=1.5))
     _log("odd slices in place %s: inorm %.3e, bn %.3e" % (shape, err_i, err_b))
     assert max(err_i, err_b) <= TOL
+
+
+# S % 4 != 0 through the read-once kernel that gives each slice one workgroup: every
+# configuration (one wave up to 1024 threads) at the edges of its range, the largest slice it
+# takes, and a full-size tensor of 31 x 31 and of 255 x 255 slices
+FLAT_SHAPES = [(5, 3, 3), (4, 5, 250), (3, 3, 1019), (2, 3, 1023), (2, 2, 4093), (2, 2, 4095),
+               (1, 3, 16381), (1, 3, 16383), (1, 2, 32767), (1, 2, 65530), (256, 64, 961),
+               (16, 64, 65025)]
+
+
+@pytest.mark.parametrize("shape", FLAT_SHAPES)
+def test_inorm_flat_read_once(dev, nra, orc, shape):
+    import torch
+
+    N, C, S = shape
+    x = synth.per_slice_affine_normal(shape, 11 + S, (0.1, 10.0), (-100.0, 100.0))
+    g = np.random.Generator(np.random.PCG64(S))
+    gamma = g.uniform(0.5, 2.0, C).astype(np.float32)
+    beta = g.uniform(-1, 1, C).astype(np.float32)
+    ref, mean, var = orc.instance_norm(x, gamma=gamma, beta=beta, with_stats=True)
+    xt = T(x, dev)
+    gt, bt = T(gamma, dev), T(beta, dev)
+    sm = torch.empty(N * C, device=dev)
+    si = torch.empty(N * C, device=dev)
+    y = nra.inorm_forward(xt, gamma=gt, beta=bt, save_mean=sm, save_invstd=si,
+                          variant=nra.NR_VARIANT_RESIDENT)
+    err = maxerr(H(y), ref)
+    y_auto = nra.inorm_forward(xt, gamma=gt, beta=bt)
+    # in place; then the same call repeated must give the same bits
+    x2 = T(x, dev)
+    nra.inorm_forward(x2, x2, gamma=gt, beta=bt, variant=nra.NR_VARIANT_RESIDENT)
+    err_in = maxerr(H(x2), ref)
+    y2 = nra.inorm_forward(xt, gamma=gt, beta=bt, variant=nra.NR_VARIANT_RESIDENT)
+    _log("inorm flat read-once %s: max_abs_err %.3e, in place %.3e" % (shape, err, err_in))
+    assert max(err, err_in, maxerr(H(y_auto), ref)) <= TOL
+    assert torch.equal(y, y2)
+    np.testing.assert_allclose(H(sm), mean.ravel(), rtol=1e-6, atol=TOL)
+    np.testing.assert_allclose(H(si), 1.0 / np.sqrt(var.ravel() + 1e-5), rtol=1e-5)
 
 
 def test_inorm_unaligned_and_side_stream(dev, nra, orc):
