@@ -84,8 +84,8 @@ nr_status inorm_forward(const float* x, float* y, int64_t N, int64_t C, int64_t 
 #define NR_VARIANT_AUTO 0     /* the library's choice for the shape */
 #define NR_VARIANT_RESIDENT 1 /* read-once: each slice held in registers, split over 1..32
                                  concurrent workgroups that exchange partial statistics; a
-                                 slice with S % 4 != 0 (S <= 65,530) is held by one
-                                 workgroup. Needs 16-byte aligned x and y */
+                                 slice with S % 4 != 0 (S <= 65,530) or S < 1024 is held by
+                                 one workgroup sized to it. Needs 16-byte aligned x and y */
 #define NR_VARIANT_SPLIT 2    /* streaming two-pass: partial statistics per chunk, a fixed-order
                                  merge, then a normalize pass (reads x twice) */
 

@@ -403,12 +403,14 @@ def test_odd_slices_in_place(dev, nra, orc, shape):
     assert max(err_i, err_b) <= TOL
 
 
-# S % 4 != 0 through the read-once kernel that gives each slice one workgroup: every
-# configuration (one wave up to 1024 threads) at the edges of its range, the largest slice it
-# takes, and a full-size tensor of 31 x 31 and of 255 x 255 slices
+# S % 4 != 0 (and S < 1024) through the read-once kernel that gives each slice one workgroup:
+# every configuration (one wave up to 1024 threads) at the edges of its range, the largest slice
+# it takes, and a full-size tensor of 31 x 31 and of 255 x 255 slices
 FLAT_SHAPES = [(5, 3, 3), (4, 5, 250), (3, 3, 1019), (2, 3, 1023), (2, 2, 4093), (2, 2, 4095),
                (1, 3, 16381), (1, 3, 16383), (1, 2, 32767), (1, 2, 65530), (256, 64, 961),
-               (16, 64, 65025)]
+               (16, 64, 65025),
+               # short aligned slices take the same kernel
+               (7, 5, 4), (1024, 64, 8), (300, 64, 256), (3, 3, 512), (5, 3, 1020)]
 
 
 @pytest.mark.parametrize("shape", FLAT_SHAPES)
