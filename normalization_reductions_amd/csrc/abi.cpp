@@ -457,7 +457,7 @@ __attribute__((visibility("default"))) nr_status inorm_forward_ex(
     // slices, which the smallest resident workgroup (256 threads) mostly leaves idle: 1.7-3.4x
     // faster up to S = 768, as fast or slower from S = 1024.
     const bool flat_ok = aligned(x, 16) && aligned(y, 16) && S <= flat_norm_max_len() &&
-                         N * C <= 0x7fffffffLL;
+                         N * C <= 0x7fffffffLL && total >= 4;
     const bool flat_pref = flat_ok && (S % 4 != 0 || S <= kFlatShortLen);
     bool use_res = false, use_flat = false;
     if (variant == NR_VARIANT_RESIDENT) {

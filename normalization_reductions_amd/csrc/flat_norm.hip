@@ -12,8 +12,10 @@
 // whole blocks t, t + BLOCK, ... in registers) and read and written with 16-byte accesses; the
 // slice's values in the partly covered first and last block (at most 3 each) are held by
 // threads 0 and 1 and read and written with 4-byte accesses. No value outside the slice is
-// touched, so every value of x is read once and every value of y written once, and in place
-// (y == x) the workgroups work on disjoint values.
+// written, and none is read except, for masked register slots, the tensor's first block: every
+// value of x is read once and every value of y written once, and in place (y == x) no
+// workgroup reads a value that another one writes. Slices of up to 67 values share a wave:
+// each takes an aligned group of 4 to 32 lanes, and "thread" above means lane of its group.
 //
 // Statistics as in the other kernels: values shifted by the slice's first value (the pivot),
 // a two-pass (mean, M2) per thread over its registers, then pairwise (Chan) merges across the
@@ -24,50 +26,58 @@
 namespace nr {
 namespace {
 
-template <int BLOCK, int VEC>
+// LANES == BLOCK: one slice per workgroup (cross-wave merge through LDS when BLOCK > 64).
+// LANES < 64: each aligned group of LANES lanes holds one slice (BLOCK / LANES slices per
+// workgroup), merged by a butterfly inside the group; no LDS, no barrier.
+template <int BLOCK, int VEC, int LANES>
 __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK, BLOCK))) void
-flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, const float* gamma,
-                 const float* beta, float* save_mean, float* save_invstd)
+flat_norm_kernel(const float* x, float* y, int64_t slices, int64_t C, int64_t S, float eps,
+                 const float* gamma, const float* beta, float* save_mean, float* save_invstd)
 {
+    constexpr bool SUB = LANES < kWave;
+    static_assert(SUB ? (BLOCK % kWave == 0 && (LANES & (LANES - 1)) == 0) : LANES == BLOCK,
+                  "a slice takes a power-of-two group inside a wave, or the whole workgroup");
     constexpr int NW = BLOCK / kWave;
-    __shared__ Stat wstat[NW];
+    __shared__ Stat wstat[SUB ? 1 : NW];
     __shared__ float coef[2];
     const int tid = threadIdx.x;
-    const int64_t s = blockIdx.x;
-    const int64_t start = s * S;
+    const int gl = SUB ? tid % LANES : tid;  // lane within the slice's group
+    const int64_t s = SUB ? (int64_t)blockIdx.x * (BLOCK / LANES) + tid / LANES : blockIdx.x;
+    const bool live = !SUB || s < slices;    // groups past the last slice only join shuffles
+    const int64_t start = live ? s * S : 0;
     const int len = (int)S;
     const int off0 = (int)(start & 3);       // the slice's first value inside its first block
     const int kw0 = off0 > 0 ? 1 : 0;        // first whole block (counted from the first block)
     const int kw1 = (off0 + len) >> 2;       // one past the last whole block
-    const int nwb = kw1 > kw0 ? kw1 - kw0 : 0;
+    const int nwb = live && kw1 > kw0 ? kw1 - kw0 : 0;
     // head: the slice's values in a partly covered first block; tail: those in a partly
     // covered last block that is not also the first
-    const int nh = off0 > 0 ? min(4, off0 + len) - off0 : 0;
-    const int nt = kw1 >= kw0 ? off0 + len - 4 * kw1 : 0;
+    const int nh = live && off0 > 0 ? min(4, off0 + len) - off0 : 0;
+    const int nt = live && kw1 >= kw0 ? off0 + len - 4 * kw1 : 0;
     const float K = x[start];
 
+    // Every load is issued unconditionally: an index past the whole blocks reads whole block 0
+    // of the slice instead (block 0 of the tensor for a slice without whole blocks or a group
+    // past the last slice; the tensor holds at least 4 values), and the value is masked below.
     const int64_t wb0 = ((start - off0) >> 2) + kw0;  // tensor block index of whole block 0
-    const f4* xw = reinterpret_cast<const f4*>(x) + wb0;
+    const f4* xv = reinterpret_cast<const f4*>(x);
     f4 v[VEC];
-    if (nwb > 0) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) v[j] = ld_stream(xw + min(j * BLOCK + tid, nwb - 1));
-    } else {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) v[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < VEC; ++j) {
+        const int i = j * LANES + gl;
+        v[j] = ld_stream(xv + (i < nwb ? wb0 + i : (nwb > 0 ? wb0 : 0)));
     }
     int ne = 0;
-    int64_t eo = start;  // first edge value of this thread
-    if (tid == 0) {
+    int64_t eo = start;  // first edge value of this lane
+    if (gl == 0) {
         ne = nh;
-    } else if (tid == 1) {
+    } else if (gl == 1) {
         ne = nt;
         eo = start + len - nt;
     }
-    float ev[3] = {0.f, 0.f, 0.f};
+    float ev[3];
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-        if (q < ne) ev[q] = ld_stream1(x + eo + q);
+    for (int q = 0; q < 3; ++q) ev[q] = ld_stream1(x + (q < ne ? eo + q : start));
 
     // Pivot-shifted values; registers past the last whole block become 0 and stay out of the
     // count.
@@ -75,7 +85,7 @@ flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, cons
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        const bool in = j * BLOCK + tid < nwb;
+        const bool in = j * LANES + gl < nwb;
         v[j] = in ? v[j] - K : f4{0.f, 0.f, 0.f, 0.f};
         cw += in;
         acc += v[j];
@@ -93,7 +103,7 @@ flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, cons
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
         const f4 d = v[j] - m;
-        qa = j * BLOCK + tid < nwb ? qa + d * d : qa;
+        qa = j * LANES + gl < nwb ? qa + d * d : qa;
     }
     float q2 = (qa.x + qa.y) + (qa.z + qa.w);
 #pragma unroll
@@ -101,31 +111,48 @@ flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, cons
         const float d = ev[q] - m;
         q2 = q < ne ? fmaf(d, d, q2) : q2;
     }
-    Stat st = wave_merge<kWave>(Stat{fn, m, q2});
-    if (lane_id() == 0) wstat[tid / kWave] = st;
-    __syncthreads();
-    if (tid < kWave) {
-        Stat w = lane_id() < NW ? wstat[lane_id()] : stat_empty();
-        w = wave_merge<NW>(w);
-        if (tid == 0) {
-            const float rstd = rsqrtf(w.m2 / w.n + eps);
-            const int64_t c = s % C;
-            const float gm = gamma ? gamma[c] : 1.f;
-            const float bt = beta ? beta[c] : 0.f;
-            const float sc = rstd * gm;
-            coef[0] = sc;
-            coef[1] = fmaf(-w.mean, sc, bt);
+    float sc, sh;
+    if (SUB) {
+        // every lane of the group ends with the slice's statistics
+        const Stat w = wave_merge<LANES>(Stat{fn, m, q2});
+        const float rstd = rsqrtf(w.m2 / w.n + eps);
+        const int64_t c = live ? s % C : 0;
+        const float gm = gamma ? gamma[c] : 1.f;
+        const float bt = beta ? beta[c] : 0.f;
+        sc = rstd * gm;
+        sh = fmaf(-w.mean, sc, bt);
+        if (live && gl == 0) {
             if (save_mean) save_mean[s] = K + w.mean;
             if (save_invstd) save_invstd[s] = rstd;
         }
+    } else {
+        const Stat st = wave_merge<kWave>(Stat{fn, m, q2});
+        if (lane_id() == 0) wstat[tid / kWave] = st;
+        __syncthreads();
+        if (tid < kWave) {
+            Stat w = lane_id() < NW ? wstat[lane_id()] : stat_empty();
+            w = wave_merge<NW>(w);
+            if (tid == 0) {
+                const float rstd = rsqrtf(w.m2 / w.n + eps);
+                const int64_t c = s % C;
+                const float gm = gamma ? gamma[c] : 1.f;
+                const float bt = beta ? beta[c] : 0.f;
+                const float scl = rstd * gm;
+                coef[0] = scl;
+                coef[1] = fmaf(-w.mean, scl, bt);
+                if (save_mean) save_mean[s] = K + w.mean;
+                if (save_invstd) save_invstd[s] = rstd;
+            }
+        }
+        __syncthreads();
+        sc = coef[0];
+        sh = coef[1];
     }
-    __syncthreads();
-    const float sc = coef[0], sh = coef[1];
-    f4* yw = reinterpret_cast<f4*>(y) + wb0;
+    f4* yv = reinterpret_cast<f4*>(y);
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        const int i = j * BLOCK + tid;
-        if (i < nwb) st_stream(yw + i, v[j] * sc + sh);
+        const int i = j * LANES + gl;
+        if (i < nwb) st_stream(yv + wb0 + i, v[j] * sc + sh);
     }
 #pragma unroll
     for (int q = 0; q < 3; ++q)
@@ -133,10 +160,13 @@ flat_norm_kernel(const float* x, float* y, int64_t C, int64_t S, float eps, cons
 }
 
 struct FlatCfg {
-    int block, vec;
+    int block, vec, lanes;
 };
-// Ascending capacity; a slice of S values spans at most (S + 6) / 4 blocks.
-constexpr FlatCfg kFlatCfgs[] = {{64, 1}, {64, 4}, {256, 4}, {256, 16}, {512, 16}, {1024, 16}};
+// Ascending capacity (lanes x vec whole blocks per slice); a slice of S values spans at most
+// (S + 6) / 4 blocks. Slices up to 67 values share waves in groups of 4 to 16 lanes.
+constexpr FlatCfg kFlatCfgs[] = {{256, 1, 4},  {256, 1, 8},  {256, 1, 16}, {256, 1, 32},
+                                 {64, 1, 64},  {64, 4, 64},  {256, 4, 256}, {256, 16, 256},
+                                 {512, 16, 512}, {1024, 16, 1024}};
 
 }  // namespace
 
@@ -146,24 +176,29 @@ hipError_t launch_flat_norm(const float* x, float* y, int64_t slices, int64_t C,
                             float eps, const float* gamma, const float* beta, float* save_mean,
                             float* save_invstd, hipStream_t stream)
 {
-    if (S < 1 || S > flat_norm_max_len() || slices < 1 || slices > 0x7fffffffLL)
+    if (S < 1 || S > flat_norm_max_len() || slices < 1 || slices > 0x7fffffffLL || slices * S < 4)
         return hipErrorInvalidValue;
     const int64_t need = (S + 6) / 4;
     for (const FlatCfg& c : kFlatCfgs) {
-        if ((int64_t)c.block * c.vec < need) continue;
-        const dim3 grid((unsigned)slices), blk(c.block);
-#define NR_FLAT(B, V)                                                                             \
-    if (c.block == B && c.vec == V) {                                                             \
-        flat_norm_kernel<B, V><<<grid, blk, 0, stream>>>(x, y, C, S, eps, gamma, beta, save_mean, \
-                                                         save_invstd);                            \
+        if ((int64_t)c.lanes * c.vec < need) continue;
+        const int64_t per = c.block / c.lanes;  // slices per workgroup
+        const dim3 grid((unsigned)((slices + per - 1) / per)), blk(c.block);
+#define NR_FLAT(B, V, L)                                                                          \
+    if (c.block == B && c.vec == V && c.lanes == L) {                                             \
+        flat_norm_kernel<B, V, L><<<grid, blk, 0, stream>>>(x, y, slices, C, S, eps, gamma, beta, \
+                                                            save_mean, save_invstd);              \
         return hipGetLastError();                                                                 \
     }
-        NR_FLAT(64, 1)
-        NR_FLAT(64, 4)
-        NR_FLAT(256, 4)
-        NR_FLAT(256, 16)
-        NR_FLAT(512, 16)
-        NR_FLAT(1024, 16)
+        NR_FLAT(256, 1, 4)
+        NR_FLAT(256, 1, 8)
+        NR_FLAT(256, 1, 16)
+        NR_FLAT(256, 1, 32)
+        NR_FLAT(64, 1, 64)
+        NR_FLAT(64, 4, 64)
+        NR_FLAT(256, 4, 256)
+        NR_FLAT(256, 16, 256)
+        NR_FLAT(512, 16, 512)
+        NR_FLAT(1024, 16, 1024)
 #undef NR_FLAT
     }
     return hipErrorInvalidValue;

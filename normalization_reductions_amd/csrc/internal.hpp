@@ -21,7 +21,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Read-once normalization: see resident.hpp.
 
 // Read-once instance normalization of slices with S % 4 != 0 (flat_norm.hip): one workgroup
-// per slice, x and y 16-byte aligned, S <= flat_norm_max_len(), slices <= 2^31 - 1.
+// per slice (or per group of 4 to 32 lanes for short slices), x and y 16-byte aligned,
+// S <= flat_norm_max_len(), slices <= 2^31 - 1, slices * S >= 4.
 int64_t flat_norm_max_len();
 hipError_t launch_flat_norm(const float* x, float* y, int64_t slices, int64_t C, int64_t S,
                             float eps, const float* gamma, const float* beta, float* save_mean,

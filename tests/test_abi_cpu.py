@@ -94,6 +94,7 @@ def _inorm(lib, x=FAKE, y=FAKE + (1 << 36), N=1, C=1, S=16, eps=1e-5, gamma=None
     (dict(variant=7), 1), (dict(ws=None), 4), (dict(wsb=16), 4), (dict(ws=FAKE + (1 << 37) + 16), 2),
     (dict(y=FAKE + 8, S=64), 1),  # partial overlap of x and y
     (dict(variant=1, S=65531), 3),  # resident variant: S % 4 != 0 only up to 65,530
+    (dict(variant=1, S=3), 3),  # ... and in a tensor of at least 4 values
     (dict(variant=1, x=FAKE + 4, y=FAKE + (1 << 36) + 4), 3),  # ... and 16-byte alignment
     (dict(variant=1, S=18, x=FAKE + 4, y=FAKE + (1 << 36) + 4), 3),  # ... for any S
     (dict(variant=1, S=32 * 32768 + 4), 3),  # ... and a slice that fits 32 parts
