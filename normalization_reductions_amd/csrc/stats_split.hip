@@ -183,9 +183,11 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
     }
 }
 
-// Flat partial step: one wave per (slice, chunk) unit, kNW units per workgroup (unit u =
-// slice * chunks + chunk, as the partial index). x is 16-byte aligned; T = slices * S < 2^32.
-template <bool CACHED, bool FINAL>
+// Flat partial step: one aligned group of LANES lanes (4..64) per (slice, chunk) unit,
+// kBlock / LANES units per workgroup (unit u = slice * chunks + chunk, as the partial index);
+// short units take narrow groups so that few lanes idle. x is 16-byte aligned;
+// T = slices * S < 2^32.
+template <bool CACHED, bool FINAL, int LANES>
 __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g, const float* x,
                                                                     const float* pre_mul,
                                                                     float2* partials, float eps,
@@ -193,9 +195,9 @@ __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g,
                                                                     float* save_mean,
                                                                     float* save_invstd, int64_t units)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t u = (int64_t)blockIdx.x * kNW + threadIdx.x / kWave;
-    if (u >= units) return;  // whole waves only: the rest of the workgroup has no barrier
+    const int lane = threadIdx.x & (LANES - 1);
+    const int64_t u = (int64_t)blockIdx.x * (kBlock / LANES) + threadIdx.x / LANES;
+    if (u >= units) return;  // whole groups only: no barrier, and shuffles stay in the group
     const int64_t slice = u / g.chunks;
     const int64_t ch = u - slice * g.chunks;
     const int64_t c = slice % g.C;
@@ -207,14 +209,14 @@ __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g,
     const int64_t b_lo = start >> 2, b_hi = (end + 3) >> 2;  // aligned blocks covering the unit
     const f4* xv = reinterpret_cast<const f4*>(x);
     Stat st = stat_empty();
-    for (int64_t b0 = b_lo; b0 < b_hi; b0 += 4 * kWave) {
+    for (int64_t b0 = b_lo; b0 < b_hi; b0 += 4 * LANES) {
         float d[16];
         bool in[16];
         int n = 0;
         float sum = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t b = b0 + j * kWave + lane;
+            const int64_t b = b0 + j * LANES + lane;
             f4 v = f4{0.f, 0.f, 0.f, 0.f};
             if (b < b_hi) {
                 if (4 * b + 3 < T) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g,
             st = chan_merge(st, Stat{fn, mean, q});
         }
     }
-    st = wave_merge<kWave>(st);
+    st = wave_merge<LANES>(st);
     if (lane == 0) {
         if (FINAL) {
             const float rstd = rsqrtf(st.m2 / st.n + eps);
@@ -394,11 +396,28 @@ void launch_partial(const SplitGeom& g, const float* x, const float* pre_mul, fl
 {
     if (split_flat(g, x, nullptr)) {
         const int64_t units = g.slices * g.chunks;
-        const dim3 gd((unsigned)((units + kNW - 1) / kNW)), bd(kBlock);
-        if (cached)
-            split_partial_flat_kernel<true, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);
-        else
-            split_partial_flat_kernel<false, FINAL><<<gd, bd, 0, stream>>>(g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);
+        // the narrowest group whose one pass (16 values a lane) covers a unit's blocks
+        const int64_t ulen = g.chunk < g.S ? g.chunk : g.S;
+        int lanes = 4;
+        while (lanes < kWave && 16 * lanes < ulen + 6) lanes *= 2;
+        const int64_t per = kBlock / lanes;
+        const dim3 gd((unsigned)((units + per - 1) / per)), bd(kBlock);
+#define NR_PFLAT(L)                                                                                \
+    if (lanes == L) {                                                                              \
+        if (cached)                                                                                \
+            split_partial_flat_kernel<true, FINAL, L><<<gd, bd, 0, stream>>>(                      \
+                g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);               \
+        else                                                                                       \
+            split_partial_flat_kernel<false, FINAL, L><<<gd, bd, 0, stream>>>(                     \
+                g, x, pre_mul, partials, eps, stats, save_mean, save_invstd, units);               \
+        return;                                                                                    \
+    }
+        NR_PFLAT(4)
+        NR_PFLAT(8)
+        NR_PFLAT(16)
+        NR_PFLAT(32)
+        NR_PFLAT(64)
+#undef NR_PFLAT
         return;
     }
     const int64_t grid = g.slices * g.chunks;

@@ -473,6 +473,8 @@ def test_inorm_unaligned_and_side_stream(dev, nra, orc):
 BN_SHAPES = [
     (128, 64, 3844),   # the Conv2d->BN workload's activation: 31 parts per channel (read-once)
     (1, 3, 1), (5, 2, 7), (64, 16, 1),  # S % 4 != 0: split path
+    # ... its statistics step in lane groups of 4 (7 x 7), 8, 16, 32 and 64 per slice
+    (128, 512, 49), (1024, 64, 3), (9, 7, 115), (5, 3, 250), (4, 5, 500), (3, 3, 1017),
     (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
     (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
     (65, 2, 32768),    # 2.1M values per channel: beyond the read-once index range -> split
