@@ -465,7 +465,7 @@ const Entry kCfgs[] = {
     NR_SINGLE(1024, 16, false, false),
     NR_PIPE(256, 8, false, false), NR_PIPE(256, 16, false, false), NR_PIPE(512, 16, false, false),
     // batch norm (groups of N slices)
-    NR_SINGLE(256, 4, true, false), NR_SINGLE(256, 16, true, false),
+    NR_SINGLE(256, 4, true, false), NR_SINGLE(256, 16, true, false), NR_SINGLE(512, 16, true, false),
     NR_PIPE(256, 16, true, false), NR_PIPE(512, 16, true, false),
     // with the chain epilogue (pre-multiply, clamp, post-multiply)
     NR_SINGLE(256, 16, false, true), NR_PIPE(256, 16, false, true), NR_PIPE(512, 16, false, true),

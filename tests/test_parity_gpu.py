@@ -476,6 +476,7 @@ BN_SHAPES = [
     # ... its statistics step in lane groups of 4 (7 x 7), 8, 16, 32 and 64 per slice
     (128, 512, 49), (1024, 64, 3), (9, 7, 115), (5, 3, 250), (4, 5, 500), (3, 3, 1017),
     (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
+    (128, 8, 196), (2, 3, 16384), (3, 2, 5464),  # ... of 512 threads (16K-32K values)
     (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
     (65, 2, 32768),    # 2.1M values per channel: beyond the read-once index range -> split
     (9, 5, 20003), (256, 64, 961),      # S % 4 != 0, flat 16-byte split path: several chunks
