@@ -411,11 +411,13 @@ FLAT_SHAPES = [(5, 3, 3), (4, 5, 250), (3, 3, 1019), (2, 3, 1023), (2, 2, 4093),
                (16, 64, 65025),
                # short aligned slices take the same kernel
                (7, 5, 4), (1024, 64, 8), (300, 64, 256), (3, 3, 512), (5, 3, 1020),
-               # slices of up to 67 values share waves in groups of 4..32 lanes (a partly
-               # filled last workgroup included): 7 x 7 at full size, each group width at the
-               # edges of its range, a single slice, and S = 1
+               # slices of up to 1018 values share workgroups in groups of 4..64 lanes (a
+               # partly filled last workgroup included): 7 x 7 at full size, each group shape
+               # at the edges of its range, a single slice, and S = 1
                (128, 512, 49), (1000, 3, 3), (9, 7, 13), (33, 3, 19), (7, 5, 35), (5, 5, 67),
-               (3, 7, 131), (1, 1, 5), (2, 2, 1)]
+               (3, 7, 131), (1, 1, 5), (2, 2, 1), (3, 3, 10), (3, 3, 11), (5, 3, 26),
+               (5, 3, 27), (3, 3, 58), (3, 3, 59), (3, 3, 122), (3, 3, 123), (3, 3, 251),
+               (3, 3, 506), (3, 3, 507), (3, 3, 1018), (128, 1024, 196)]
 
 
 @pytest.mark.parametrize("shape", FLAT_SHAPES)
