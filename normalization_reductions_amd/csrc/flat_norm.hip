@@ -1,7 +1,8 @@
 // flat_norm.hip -- read-once instance normalization for slices whose length is not a multiple
 // of 4, in a 16-byte aligned tensor: apart from the first, such slices start off 16-byte
 // boundaries, so the read-once kernels of resident_norm.hip (16-byte accesses from each slice's
-// start) do not apply.
+// start) do not apply. Short aligned slices (fewer than 1024 values) take it too: it sizes the
+// lanes to the slice, where the smallest resident workgroup (256 threads) would mostly idle.
 //
 // IN2d page, statement of the op (and the IN3d page's InstanceNorm3d reading): per (n, c) slice
 // of S values, mean and biased variance over the slice, y = (x - mean) / sqrt(var + eps), then
@@ -15,8 +16,8 @@
 // written, and none is read except, for masked register slots, the tensor's first block: every
 // value of x is read once and every value of y written once, and in place (y == x) no
 // workgroup reads a value that another one writes. Slices of up to 1018 values share a
-// workgroup: each takes an aligned group of 4 to 64 lanes (up to 67 values, several share a
-// wave), and "thread" above means lane of its group.
+// 256-thread workgroup: each takes an aligned group of 4 to 64 lanes (several groups to a wave
+// below 64 lanes), and "thread" above means lane of its group.
 //
 // Statistics as in the other kernels: values shifted by the slice's first value (the pivot),
 // a two-pass (mean, M2) per thread over its registers, then pairwise (Chan) merges across the
