@@ -542,6 +542,15 @@ __attribute__((visibility("default"))) nr_status bn_train_forward_ex(
     size_t off_x, off_p, off_s;
     const size_t need = bn_layout(N, C, S, vec, &g, &off_x, &off_p, &off_s);
     if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
+    // slices off 16-byte boundaries, channels that one workgroup holds: read once (flat_norm.hip)
+    if (S % 4 != 0 && aligned(x, 16) && aligned(y, 16) && flat_bn_fits(N, C, S) &&
+        C <= 0x7fffffffLL && total >= 4) {
+        const hipError_t e = launch_flat_bn(x, y, N, C, S, eps, gamma, beta, out_scale, save_mean,
+                                            save_invstd, running_mean, running_var, momentum,
+                                            stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     int cfg_idx = -1, P = 0;
     if (vec && choose_resident(N * S, true, false, &cfg_idx, &P) && (P == 1 || off_x != 0) &&
         C * P <= 0xF0000000LL && C <= 0x7fffffffLL) {

@@ -24,6 +24,14 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // per slice (or per group of 4 to 32 lanes for short slices), x and y 16-byte aligned,
 // S <= flat_norm_max_len(), slices <= 2^31 - 1, slices * S >= 4.
 int64_t flat_norm_max_len();
+// Read-once training-mode batch norm of slices with S % 4 != 0 (flat_norm.hip): one workgroup
+// per channel when the channel's N slices fit it and all C workgroups are resident at once
+// (flat_bn_fits); x and y 16-byte aligned, C <= 2^31 - 1, N * C * S >= 4.
+bool flat_bn_fits(int64_t N, int64_t C, int64_t S);
+hipError_t launch_flat_bn(const float* x, float* y, int64_t N, int64_t C, int64_t S, float eps,
+                          const float* gamma, const float* beta, float out_scale,
+                          float* save_mean, float* save_invstd, float* running_mean,
+                          float* running_var, float momentum, hipStream_t stream);
 hipError_t launch_flat_norm(const float* x, float* y, int64_t slices, int64_t C, int64_t S,
                             float eps, const float* gamma, const float* beta, float* save_mean,
                             float* save_invstd, hipStream_t stream);

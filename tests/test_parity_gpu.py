@@ -475,8 +475,11 @@ def test_inorm_unaligned_and_side_stream(dev, nra, orc):
 BN_SHAPES = [
     (128, 64, 3844),   # the Conv2d->BN workload's activation: 31 parts per channel (read-once)
     (1, 3, 1), (5, 2, 7), (64, 16, 1),  # S % 4 != 0: split path
-    # ... its statistics step in lane groups of 4 (7 x 7), 8, 16, 32 and 64 per slice
-    (128, 512, 49), (1024, 64, 3), (9, 7, 115), (5, 3, 250), (4, 5, 500), (3, 3, 1017),
+    # ... or, where one workgroup holds a channel, read once in lane groups (each group
+    # shape, with live and empty groups); the split statistics step in lane groups of 4 to 64
+    (128, 512, 49), (9, 7, 115), (5, 3, 250), (4, 5, 500), (3, 3, 1017), (512, 3, 9),
+    (513, 3, 9), (129, 3, 49), (17, 3, 250), (1024, 64, 3), (33, 3, 500), (256, 4, 121),
+    (8, 2048, 49),  # more channels than resident workgroups: the split path
     (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
     (128, 8, 196), (2, 3, 16384), (3, 2, 5464),  # ... of 512 threads (16K-32K values)
     (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
@@ -528,7 +531,7 @@ def test_bn_train_large_offset_small_spread(dev, nra, orc, shape):
 # running statistics: resident single-workgroup, pipelined, split (S % 4 != 0) and the
 # beyond-index-range split path; two steps in a row so the update compounds
 BN_RUNNING_SHAPES = [(128, 64, 3844), (5, 2, 7), (2, 4, 4100), (33, 2, 16000), (65, 2, 32768),
-                     (9, 5, 20003)]
+                     (9, 5, 20003), (128, 32, 49), (3, 3, 1017)]
 
 
 def _check_running(rm_gpu, rv_gpu, rm_ref, rv_ref, what):
