@@ -480,6 +480,7 @@ BN_SHAPES = [
     (128, 512, 49), (9, 7, 115), (5, 3, 250), (4, 5, 500), (3, 3, 1017), (512, 3, 9),
     (513, 3, 9), (129, 3, 49), (17, 3, 250), (1024, 64, 3), (33, 3, 500), (256, 4, 121),
     (8, 2048, 49),  # more channels than resident workgroups: the split path
+    (256, 8, 49), (257, 3, 49),  # more slices per channel than a workgroup holds: split path
     (2, 4, 4100), (7, 3, 1000),          # one workgroup per channel
     (128, 8, 196), (2, 3, 16384), (3, 2, 5464),  # ... of 512 threads (16K-32K values)
     (3, 1, 100000), (33, 2, 16000), (1, 5, 65536),  # pipelined: ragged, 17 and 4 parts
