@@ -249,9 +249,12 @@ def conv_norm_epilogue_forward(x, w, b=None, out=None, *, norm=NR_NORM_BATCH_TRA
         raise ValueError("out must have shape %s" % (oshape,))
     need = conv_norm_epilogue_workspace_size(d)
     if need == 0:
+        # no workspace (an empty batch) -- or a descriptor the size query rejects, which this
+        # call then reports
         check(lib.conv_norm_epilogue_forward(ctypes.byref(d), x.data_ptr(), w.data_ptr(), bp,
                                              out.data_ptr(), None, 0, _stream(x.device, stream)),
               "conv_norm_epilogue_forward")
+        return out
     ws = workspace if workspace is not None else get_workspace(need, x.device, stream)
     check(lib.conv_norm_epilogue_forward(ctypes.byref(d), x.data_ptr(), w.data_ptr(), bp,
                                          out.data_ptr(), ctypes.c_void_p(ws.data_ptr()),

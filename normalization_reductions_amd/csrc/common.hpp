@@ -43,6 +43,21 @@ __device__ __forceinline__ Stat chan_merge(Stat a, Stat b)
     return r;
 }
 
+// Rounded product that the compiler may not fuse into a following add. A chain's statistics
+// and its normalize step both form u = c * pre_mul; on a constant channel (variance 0, so the
+// deviation is multiplied by 1/sqrt(eps)) the two must round u the same way, and a fused
+// fma(c, pm, -mean) keeps the product's rounding error that the statistics' mean dropped.
+__device__ __forceinline__ float mul_rn(float a, float b)
+{
+#pragma clang fp contract(off)
+    return a * b;
+}
+__device__ __forceinline__ f4 mul_rn(f4 a, float b)
+{
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Butterfly over lane distances 1 .. WIDTH/2 (WIDTH a power of two <= 64). After it, every

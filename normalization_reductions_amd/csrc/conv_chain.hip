@@ -146,7 +146,9 @@ __host__ __device__ inline int64_t ring_wg_of(int64_t t, int64_t total, int64_t 
 
 // Chan's merge of a step's statistics b (b.n > 0) into a lane's running statistics a, with the
 // hardware reciprocal (1 ulp) for the weight: it runs once per tile step, inside the matrix
-// loop. The exact merge (chan_merge) combines lanes, waves and workgroups.
+// loop. The exact merge (chan_merge) combines lanes, waves and workgroups. An empty a takes b
+// as it is (the reciprocal's weight would round b's mean), and equal means merge exactly, so
+// a constant channel keeps its value as the mean.
 __device__ __forceinline__ Stat merge_step(Stat a, Stat b)
 {
     Stat r;
@@ -155,28 +157,30 @@ __device__ __forceinline__ Stat merge_step(Stat a, Stat b)
     const float d = b.mean - a.mean;
     r.mean = fmaf(d, f, a.mean);
     r.m2 = a.m2 + b.m2 + d * d * a.n * f;
-    return r;
+    return a.n > 0.f ? r : b;
 }
 
-// Two-pass statistics of V values (all valid), summed as a tree.
+// Two-pass statistics of V values (all valid), shifted by the first (the pivot) and summed as
+// a tree: the mean is pivot + mean of the shifted values, exactly the value on a constant tile.
 template <int V>
 __device__ __forceinline__ Stat tile_stat(const float* v)
 {
+    const float K = v[0];
     float t[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) t[i] = v[i];
+    for (int i = 0; i < V; ++i) t[i] = v[i] - K;
 #pragma unroll
     for (int w = 1; w < V; w <<= 1)
 #pragma unroll
         for (int i = 0; i + w < V; i += 2 * w) t[i] += t[i + w];
-    const float mean = t[0] * (1.f / V);
+    const float md = t[0] * (1.f / V);
 #pragma unroll
-    for (int i = 0; i < V; ++i) t[i] = (v[i] - mean) * (v[i] - mean);
+    for (int i = 0; i < V; ++i) t[i] = (v[i] - K - md) * (v[i] - K - md);
 #pragma unroll
     for (int w = 1; w < V; w <<= 1)
 #pragma unroll
         for (int i = 0; i + w < V; i += 2 * w) t[i] += t[i + w];
-    return Stat{(float)V, mean, t[0]};
+    return Stat{(float)V, K + md, t[0]};
 }
 
 // Statistics of one tile step, from the lane's valid values. Planar: channel ch at positions
@@ -191,16 +195,14 @@ __device__ __forceinline__ void ring_tile_stats(const mf4* acc, int t0, int thi,
     if (CL) {
         // channels last: MT values per channel and step, too few for a merge each; shifted sums
         // instead (run[r] holds the shift K in .mean, the sums of (v - K) and (v - K)^2 in .m2
-        // and sh[r]), the shift being the lane's first step mean, so |mean - K| stays within a
-        // few standard deviations and the final M2 = S2 - S1^2 / n loses little
+        // and sh[r]), the shift being the lane's first value of the channel, so |mean - K|
+        // stays within a few standard deviations, the final M2 = S2 - S1^2 / n loses little,
+        // and a constant channel gives S1 = S2 = 0 and the value itself as the mean
         const bool first = run[0].n == 0.f;
         if (whole) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float m = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) m += acc[mt][r];
-                const float K = first ? m * (1.f / MT) : run[r].mean;
+                const float K = first ? acc[0][r] : run[r].mean;
                 float s1 = 0.f, s2 = 0.f;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -223,13 +225,12 @@ __device__ __forceinline__ void ring_tile_stats(const mf4* acc, int t0, int thi,
             cnt += ok[mt];
         }
         if (cnt == 0) return;
-        const float inv = __builtin_amdgcn_rcpf((float)cnt);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float m = 0.f;
+            float first_v = 0.f;  // the lane's first valid value of channel 4q + r in this step
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) m += ok[mt] ? acc[mt][r] : 0.f;
-            const float K = first ? m * inv : run[r].mean;
+            for (int mt = MT - 1; mt >= 0; --mt) first_v = ok[mt] ? acc[mt][r] : first_v;
+            const float K = first ? first_v : run[r].mean;
             float s1 = 0.f, s2 = 0.f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -256,28 +257,33 @@ __device__ __forceinline__ void ring_tile_stats(const mf4* acc, int t0, int thi,
     }
     bool ok[MT][4];
     int cnt = 0;
-    float s = 0.f;
+    float K = 0.f;  // pivot: the first valid value
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = MT - 1; mt >= 0; --mt) {
         const int p0 = (t0 + mt) * 16 + 4 * q - shift;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 3; r >= 0; --r) {
             ok[mt][r] = t0 + mt < thi && p0 + r >= 0 && p0 + r < inner_out;
             cnt += ok[mt][r];
-            s += ok[mt][r] ? acc[mt][r] : 0.f;
+            K = ok[mt][r] ? acc[mt][r] : K;
         }
     }
     if (cnt == 0) return;
-    const float mean = s / (float)cnt;
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += ok[mt][r] ? acc[mt][r] - K : 0.f;
+    const float md = s / (float)cnt;
     float m2 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float d = ok[mt][r] ? acc[mt][r] - mean : 0.f;
+            const float d = ok[mt][r] ? acc[mt][r] - K - md : 0.f;
             m2 = fmaf(d, d, m2);
         }
-    run[0] = merge_step(run[0], Stat{(float)cnt, mean, m2});
+    run[0] = merge_step(run[0], Stat{(float)cnt, K + md, m2});
 }
 
 __device__ __forceinline__ Stat shfl_xor_stat(Stat s, int off)
@@ -329,7 +335,7 @@ __device__ __forceinline__ void ring_stats_flush(const ConvGeom& g, const ConvRi
         for (int m = 1; m < WAVES_M; ++m) st = chan_merge(st, red[m * (int)g.Cout + k]);
         const float pm = rs.pre_mul ? rs.pre_mul[k] : 1.f;
         float4* slot = rs.part + (n * rs.J) * g.Cout + k;
-        slot[j * g.Cout] = make_float4(st.n, st.mean * pm, st.m2 * pm * pm, 0.f);
+        slot[j * g.Cout] = make_float4(st.n, mul_rn(st.mean, pm), st.m2 * pm * pm, 0.f);
         if (last)
             for (int64_t jj = j + 1; jj < rs.J; ++jj) slot[jj * g.Cout] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -776,26 +782,20 @@ __device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsign
 // output ((v - mean) * rstd * gamma + beta) * out_scale, clamped, times post_mul, in the order
 // the chain epilogue uses.
 //
-// For channels of at least kC8StatsTwoParts values the statistics pass splits x into two
-// parts and forms hh, hm, mh and x_h w_l (four products for six): each conv value is then off
-// by up to ~3e-5 of its scale, but that error comes from the rounding of x, which varies from
-// position to position and averages out of a channel's mean and variance (emulated on the CPU
-// and measured: ~2e-7 relative, at the rounding of the fp32 sums). W keeps three parts: its
-// rounding error would be the same at every position and would bias the variance (by ~2e-6
-// with two parts). Smaller channels, where too few values average, use all six products.
-constexpr int64_t kC8StatsTwoParts = 16384;
+// The statistics pass forms the same six products, in the same order, as the apply pass, so
+// its statistics are those of the very values the apply pass normalizes. That matters on a
+// channel of (near) zero variance, where any difference between the two passes' values is
+// multiplied by 1/sqrt(eps): a constant input must give exactly beta * out_scale (BN page,
+// opening training-mode analysis).
 enum { kC8Conv = 0, kC8Stats = 1, kC8Apply = 2 };
 
-template <int B, int MODE, int NS>
+template <int B, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const float* __restrict__ w,
                              const float* __restrict__ b, float* __restrict__ c, C8Chain e)
 {
     constexpr int W = kC8W, OW = W - 2;
-    // NS: bf16 parts of each x value in the staged windows. Three (products hh, hm, mh, mm, hl,
-    // lh: fp32 accuracy) wherever conv values are stored; two (products hh, hm, mh and x_h w_l)
-    // for the statistics of large channels. W always has three.
-    static_assert(NS == 3 || (NS == 2 && MODE == kC8Stats), "two parts only for statistics");
+    constexpr int NS = 3;                          // bf16 parts of each staged x value
     constexpr int ROWS = B + 2;                    // input rows a box reads
     constexpr int SPLIT = ROWS * W * kC8Cin;       // bf16 of one split of a staged window
     constexpr int WIN = NS * SPLIT;                // bf16 of one staged window
@@ -889,8 +889,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 unsigned short* d = win + buf * WIN + (srow * W + 4 * sj + e) * kC8Cin + 4 * scq;
                 *reinterpret_cast<mu2*>(d) = mu2{h[0] | h[1] << 16, h[2] | h[3] << 16};
                 *reinterpret_cast<mu2*>(d + SPLIT) = mu2{mm[0] | mm[1] << 16, mm[2] | mm[3] << 16};
-                if (NS == 3)
-                    *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
+                *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
             }
         }
     };
@@ -936,13 +935,11 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 const unsigned short* a = q == 1 ? a2 : q == 4 ? a0 : a1;
                 const bf8 ah = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off));
                 const bf8 am = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + SPLIT));
-                if (NS == 3) {
-                    const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + (NS - 1) * SPLIT));
-                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][1], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][1], acc1, 0, 0, 0);
-                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[0][q][0], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[1][q][0], acc1, 0, 0, 0);
-                }
+                const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + 2 * SPLIT));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[0][q][1], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[0][q][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wb[1][q][0], acc1, 0, 0, 0);
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][2], acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][2], acc1, 0, 0, 0);
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][1], acc0, 0, 0, 0);
@@ -957,48 +954,58 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 // last tile starts earlier), none for a repeated tile
                 const int t = wave + 4 * i;
                 const int own = t < tiles ? 32 * t : BP;
-                // statistics of the raw sums; the bias and pre-multiplier enter once per
-                // workgroup (mean (m + b) * pm, M2 * pm^2) when the partial is written
+                // statistics of the raw sums, shifted by the lane's first owned value (so a
+                // constant channel gives exactly that value as its mean); the bias and
+                // pre-multiplier enter once per workgroup (mean (m + b) * pm, M2 * pm^2) when
+                // the partial is written, rounded as the apply pass rounds each value
                 const mf16& v0 = acc0;
                 const mf16& v1 = acc1;
                 if (ts == own) {  // the whole tile is owned (all but a box's last or repeated tiles)
+                    const float K0 = v0[0], K1 = v1[0];
                     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        s0 += v0[r];
-                        s1 += v1[r];
+                        s0 += v0[r] - K0;
+                        s1 += v1[r] - K1;
                     }
-                    const float mean0 = s0 * 0.0625f, mean1 = s1 * 0.0625f;
+                    const float md0 = s0 * 0.0625f, md1 = s1 * 0.0625f;
                     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        d0 = fmaf(v0[r] - mean0, v0[r] - mean0, d0);
-                        d1 = fmaf(v1[r] - mean1, v1[r] - mean1, d1);
+                        d0 = fmaf(v0[r] - K0 - md0, v0[r] - K0 - md0, d0);
+                        d1 = fmaf(v1[r] - K1 - md1, v1[r] - K1 - md1, d1);
                     }
-                    run0 = chan_merge(run0, Stat{16.f, mean0, d0});
-                    run1 = chan_merge(run1, Stat{16.f, mean1, d1});
+                    run0 = chan_merge(run0, Stat{16.f, K0 + md0, d0});
+                    run1 = chan_merge(run1, Stat{16.f, K1 + md1, d1});
                     continue;
                 }
                 int cnt = 0;
-                float s0 = 0.f, s1 = 0.f;
+                float K0 = 0.f, K1 = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 15; r >= 0; --r) {
                     const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
                     cnt += in;
-                    s0 += in ? v0[r] : 0.f;
-                    s1 += in ? v1[r] : 0.f;
+                    K0 = in ? v0[r] : K0;
+                    K1 = in ? v1[r] : K1;
                 }
                 if (cnt > 0) {
-                    const float fn = (float)cnt, mean0 = s0 / fn, mean1 = s1 / fn;
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
+                        s0 += in ? v0[r] - K0 : 0.f;
+                        s1 += in ? v1[r] - K1 : 0.f;
+                    }
+                    const float fn = (float)cnt, md0 = s0 / fn, md1 = s1 / fn;
                     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
-                        d0 = in ? fmaf(v0[r] - mean0, v0[r] - mean0, d0) : d0;
-                        d1 = in ? fmaf(v1[r] - mean1, v1[r] - mean1, d1) : d1;
+                        d0 = in ? fmaf(v0[r] - K0 - md0, v0[r] - K0 - md0, d0) : d0;
+                        d1 = in ? fmaf(v1[r] - K1 - md1, v1[r] - K1 - md1, d1) : d1;
                     }
-                    run0 = chan_merge(run0, Stat{fn, mean0, d0});
-                    run1 = chan_merge(run1, Stat{fn, mean1, d1});
+                    run0 = chan_merge(run0, Stat{fn, K0 + md0, d0});
+                    run1 = chan_merge(run1, Stat{fn, K1 + md1, d1});
                 }
             } else {
 #pragma unroll
@@ -1007,8 +1014,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                     mf4 z0 = mf4{acc0[4 * j], acc0[4 * j + 1], acc0[4 * j + 2], acc0[4 * j + 3]} + bias0;
                     mf4 z1 = mf4{acc1[4 * j], acc1[4 * j + 1], acc1[4 * j + 2], acc1[4 * j + 3]} + bias1;
                     if (MODE == kC8Apply) {
-                        z0 = (z0 * pm0 - mu0) * A0 + B0;
-                        z1 = (z1 * pm1 - mu1) * A1 + B1;
+                        z0 = (mul_rn(z0, pm0) - mu0) * A0 + B0;
+                        z1 = (mul_rn(z1, pm1) - mu1) * A1 + B1;
                         if (e.clamp) {
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
@@ -1051,7 +1058,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
             for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + ch]);
             const float bc = b ? b[ch] : 0.f, pc = e.pre_mul ? e.pre_mul[ch] : 1.f;
-            e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, (t.mean + bc) * pc, t.m2 * pc * pc, 0.f};
+            e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, mul_rn(t.mean + bc, pc), t.m2 * pc * pc, 0.f};
         }
     }
 }
@@ -1113,7 +1120,7 @@ __device__ __forceinline__ float chain_value(const ChainArgs& a, int64_t n, int6
     const float pm = a.pre_mul ? a.pre_mul[k] : 1.f;
     const float A = s.rstd * (a.gamma ? a.gamma[k] : 1.f) * a.out_scale;
     const float B = (a.beta ? a.beta[k] : 0.f) * a.out_scale;
-    float z = ((cv * pm - s.pivot) - s.mean_d) * A + B;
+    float z = ((mul_rn(cv, pm) - s.pivot) - s.mean_d) * A + B;
     if (a.clamp) z = fminf(fmaxf(z, a.lo), a.hi);
     if (a.post_mul) z *= a.post_mul[k];
     return z;
@@ -1137,7 +1144,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_vec_kernel(ChainArgs 
         const float B = (a.beta ? a.beta[k] : 0.f) * a.out_scale;
         const float qm = a.post_mul ? a.post_mul[k] : 1.f;
         const f4 cv = cp[k * plane4];  // plain load: the statistics pass just read these lines
-        f4 z = ((cv * pm - s.pivot) - s.mean_d) * A + B;
+        f4 z = ((mul_rn(cv, pm) - s.pivot) - s.mean_d) * A + B;
         if (a.clamp) {
             z.x = fminf(fmaxf(z.x, a.lo), a.hi);
             z.y = fminf(fmaxf(z.y, a.lo), a.hi);
@@ -1213,7 +1220,7 @@ __global__ __launch_bounds__(kChainBlock) void chain_apply_slots_kernel(ChainArg
     f4 m = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     auto one = [&](int k, f4 cv) {
         const float4 q = coef[k];
-        f4 z = (cv * q.x - q.y) * q.z + q.w;
+        f4 z = (mul_rn(cv, q.x) - q.y) * q.z + q.w;
         if (a.clamp) {
             z.x = fminf(fmaxf(z.x, a.lo), a.hi);
             z.y = fminf(fmaxf(z.y, a.lo), a.hi);
@@ -1414,16 +1421,13 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
                                      float eps, RunningStats run, hipStream_t stream)
 {
     const int64_t G = c8_grid(g);
-    if (g.N * g.SP >= kC8StatsTwoParts)
-        conv2d_c8_bf16x6_kernel<kC8B, kC8Stats, 2><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
-    else
-        conv2d_c8_bf16x6_kernel<kC8B, kC8Stats, 3><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Stats><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     c8_stats_merge_kernel<<<dim3((unsigned)g.Cout), dim3(kWave), 0, stream>>>(e.part, (int)G, eps, stats, run);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     e.stats = stats;
-    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply, 3><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
     return hipGetLastError();
 }
 
@@ -1443,7 +1447,7 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
             if (conv_fp32_forced())
                 conv2d_c8_mfma32_kernel<kC8B><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(g, x, w, b, c);
             else
-                conv2d_c8_bf16x6_kernel<kC8B, kC8Conv, 3><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+                conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
                     g, x, w, b, c, C8Chain{});
             return hipGetLastError();
         }

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, cons
     const int64_t ch = wg - slice * g.chunks;
     const int64_t c = slice % g.C;
     const float m = pre_mul ? pre_mul[c] : 1.f;
-    const float K = x[pivot_slice(group_of(g, slice)) * g.S] * m;
+    const float K = mul_rn(x[pivot_slice(group_of(g, slice)) * g.S], m);
     const int64_t start = ch * g.chunk;
     const int64_t len = chunk_len(g, ch);
     const float* xs = x + slice * g.S + start;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, cons
                 const int64_t i = i0 + j * kBlock + tid;
                 f4 t = f4{0.f, 0.f, 0.f, 0.f};
                 if (i < nv) {
-                    t = (CACHED ? xv[i] : ld_stream(xv + i)) * m - K;
+                    t = mul_rn(CACHED ? xv[i] : ld_stream(xv + i), m) - K;
                     n += 4;
                 }
                 d[4 * j + 0] = t.x;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_kernel(SplitGeom g, cons
                 const int64_t i = i0 + j * kBlock + tid;
                 d[j] = 0.f;
                 if (i < len) {
-                    d[j] = (CACHED ? xs[i] : ld_stream1(xs + i)) * m - K;
+                    d[j] = mul_rn(CACHED ? xs[i] : ld_stream1(xs + i), m) - K;
                     ++n;
                 }
             }
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kWave) void split_merge_kernel(SplitGeom g, const f
     if (lane == 0) {
         const int64_t c = grp % g.C;
         const float m = pre_mul ? pre_mul[c] : 1.f;
-        const float K = x[pivot_slice(grp) * g.S] * m;
+        const float K = mul_rn(x[pivot_slice(grp) * g.S], m);
         const float rstd = rsqrtf(st.m2 / st.n + eps);
         stats[grp] = GroupStat{K, st.mean, rstd, 0.f};
         if (save_mean) save_mean[grp] = K + st.mean;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g,
     const int64_t ch = u - slice * g.chunks;
     const int64_t c = slice % g.C;
     const float m = pre_mul ? pre_mul[c] : 1.f;
-    const float K = x[pivot_slice(group_of(g, slice)) * g.S] * m;
+    const float K = mul_rn(x[pivot_slice(group_of(g, slice)) * g.S], m);
     const int64_t T = g.slices * g.S;
     const int64_t start = slice * g.S + ch * g.chunk;
     const int64_t end = start + chunk_len(g, ch);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void split_partial_flat_kernel(SplitGeom g,
                 const int64_t i = 4 * b + e;
                 const bool ok = b < b_hi && i >= start && i < end;
                 in[4 * j + e] = ok;
-                d[4 * j + e] = ok ? fmaf(v[e], m, -K) : 0.f;
+                d[4 * j + e] = ok ? mul_rn(v[e], m) - K : 0.f;
                 n += ok;
                 sum += d[4 * j + e];
             }
