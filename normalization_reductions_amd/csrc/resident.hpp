@@ -52,6 +52,10 @@ struct ResidentArgs {
     uint32_t* counter;           // next unit to take; followed (256 B on) by the slots
     unsigned long long* slots;   // [groups][P][2] tagged exchange words
     uint32_t* flags;             // sticky error word
+    // set by launch_resident: the tag an exchange wait accepts and its polling bound (the tag
+    // the parts publish and kSpinLimit, except under the give-up test switch)
+    uint32_t wait_tag;
+    uint32_t spin_limit;
 };
 
 uint64_t resident_div_magic(int64_t S);
