@@ -96,6 +96,18 @@ nr_status inorm_forward_ex(const float* x, float* y, int64_t N, int64_t C, int64
                            float* save_invstd, void* workspace, size_t workspace_bytes,
                            int variant, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): inorm_forward with the library's own workspace, a
+ * device array of 8 MiB (8388608 bytes) that the library holds on every GPU it runs on until
+ * the process ends. Arguments as inorm_forward. Shapes whose inorm_workspace_size exceeds
+ * 8 MiB are rejected with NR_ERR_WORKSPACE (x[112,64,512,512] needs 3.7 MiB). Nothing is
+ * allocated or freed: the array's address is looked up once per device, on the first call
+ * with that device current. Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (two streams, or threads without ordering) race; order them. */
+nr_status inorm_forward_noalloc(const float* x, float* y, int64_t N, int64_t C, int64_t S,
+                                float eps, const float* gamma, const float* beta,
+                                float* save_mean, float* save_invstd, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Training-mode batch normalization, then a scale.
  *

@@ -143,6 +143,25 @@ def inorm_forward(x, y=None, *, eps: float = 1e-5, gamma=None, beta=None, save_m
     return y
 
 
+def inorm_forward_noalloc(x, y, *, eps: float = 1e-5, gamma=None, beta=None, save_mean=None,
+                          save_invstd=None, stream=None):
+    """inorm_forward with the library's own 8 MiB device workspace: the call allocates nothing
+    (y must be given). Calls that overlap on one GPU race (see normred.h)."""
+    lib = _lib.load()
+    _dev_f32(x, "x")
+    N, C, S = _nc_s(x)
+    _dev_f32(y, "y")
+    if y.shape != x.shape or y.device != x.device:
+        raise ValueError("y must match x in shape and device")
+    g = _opt_ptr(gamma, "gamma", C, x.device)
+    b = _opt_ptr(beta, "beta", C, x.device)
+    sm = _opt_ptr(save_mean, "save_mean", N * C, x.device)
+    si = _opt_ptr(save_invstd, "save_invstd", N * C, x.device)
+    check(lib.inorm_forward_noalloc(x.data_ptr(), y.data_ptr(), N, C, S, float(eps), g, b, sm, si,
+                                    _stream(x.device, stream)), "inorm_forward_noalloc")
+    return y
+
+
 # ---------------------------------------------------------------------------------------------
 # Batch norm (training mode)
 # ---------------------------------------------------------------------------------------------

@@ -67,6 +67,7 @@ SIGNATURES = {
     "inorm_forward": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "inorm_forward_ex": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _vp, _vp, _vp, _sz, _i,
                               _vp]),
+    "inorm_forward_noalloc": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _vp, _vp, _vp]),
     "bn_train_workspace_size": (_sz, [_i64, _i64, _i64]),
     "bn_train_forward": (_i, [_vp, _vp, _i64, _i64, _i64, _f, _vp, _vp, _f, _vp, _vp, _vp, _sz,
                               _vp]),

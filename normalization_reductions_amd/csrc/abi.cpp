@@ -31,6 +31,21 @@ nr_status fail(nr_status s, const char* fmt, ...)
     return s;
 }
 
+}  // namespace
+
+nr_status nr::set_error(nr_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return s;
+}
+
+namespace {
+
 nr_status hip_fail(hipError_t e, const char* where)
 {
     return fail(NR_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));

@@ -6,9 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "normred.h"
 #include "resident.hpp"
 
 namespace nr {
+
+// Records the message nr_last_error() returns on this thread and returns s (abi.cpp).
+nr_status set_error(nr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // ---------------------------------------------------------------------------------------------
 // Workspace regions (byte offsets inside the caller's workspace; every region 256-B aligned).
