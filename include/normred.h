@@ -266,6 +266,14 @@ nr_status nr_workspace_check(void* workspace, size_t bytes, hipStream_t stream, 
  * path. */
 nr_status nr_stream_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 
+/* The same copy in the fastest pattern measured on MI355X: one persistent workgroup per CU
+ * taking 64 KiB units in order from a counter kept in `workspace` (>= 256 bytes, 256-byte
+ * aligned; its first 4 bytes are zeroed on `stream` and then used). Vector path under the same
+ * conditions as nr_stream_copy, which serves every other call. Calls sharing a workspace must
+ * be ordered. */
+nr_status nr_stream_copy_ws(const float* src, float* dst, int64_t n, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -312,12 +312,20 @@ def conv_bn_eval_forward(x, w, b, running_mean, running_var, out=None, *, eps=1e
     return out
 
 
-def stream_copy(src, dst, stream=None):
+def stream_copy(src, dst, stream=None, workspace=None):
+    """dst <- src with the library's streaming copy; with a workspace (>= 256 bytes), the
+    persistent copy that takes its units from a counter there."""
     lib = _lib.load()
     _dev_f32(src, "src")
     _dev_f32(dst, "dst")
     if src.numel() != dst.numel():
         raise ValueError("src and dst sizes differ")
-    check(lib.nr_stream_copy(src.data_ptr(), dst.data_ptr(), src.numel(),
-                             _stream(src.device, stream)), "nr_stream_copy")
+    if workspace is None:
+        check(lib.nr_stream_copy(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                 _stream(src.device, stream)), "nr_stream_copy")
+    else:
+        check(lib.nr_stream_copy_ws(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                    ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(src.device, stream)), "nr_stream_copy_ws")
     return dst

@@ -82,6 +82,7 @@ SIGNATURES = {
     "nr_workspace_clear": (_i, [_vp, _sz, _vp]),
     "nr_workspace_check": (_i, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "nr_stream_copy": (_i, [_vp, _vp, _i64, _vp]),
+    "nr_stream_copy_ws": (_i, [_vp, _vp, _i64, _vp, _sz, _vp]),
 }
 
 _lib = None

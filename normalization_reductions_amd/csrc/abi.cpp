@@ -836,4 +836,23 @@ __attribute__((visibility("default"))) nr_status nr_stream_copy(const float* src
     return NR_OK;
 }
 
+__attribute__((visibility("default"))) nr_status nr_stream_copy_ws(const float* src, float* dst,
+                                                                   int64_t n, void* workspace,
+                                                                   size_t workspace_bytes,
+                                                                   hipStream_t stream)
+{
+    static const char* fn = "nr_stream_copy_ws";
+    if (!src || !dst || n < 0) return fail(NR_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    if (!aligned(src, 4) || !aligned(dst, 4)) return fail(NR_ERR_MISALIGNED, "%s: misaligned", fn);
+    if (ranges_partially_overlap(src, dst, n) || (src == dst && n > 0))
+        return fail(NR_ERR_INVALID_ARG, "%s: src and dst overlap", fn);
+    if (!workspace || workspace_bytes < 256 || !aligned(workspace, 256))
+        return fail(NR_ERR_WORKSPACE, "%s: needs a 256-byte aligned workspace of >= 256 bytes", fn);
+    const bool vec = aligned(src, 16) && aligned(dst, 16) && n % 4 == 0;
+    const hipError_t e = vec ? launch_stream_copy_persistent(src, dst, n, workspace, stream)
+                             : launch_stream_copy(src, dst, n, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return NR_OK;
+}
+
 }  // extern "C"

@@ -211,5 +211,8 @@ hipError_t launch_cl_apply(const ChainArgs& a, const ClGeom& g, const float4* pa
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+// Persistent copy (src, dst 16-byte aligned, n % 4 == 0); counter: 4 device bytes it zeroes.
+hipError_t launch_stream_copy_persistent(const float* src, float* dst, int64_t n, void* counter,
+                                         hipStream_t stream);
 
 }  // namespace nr

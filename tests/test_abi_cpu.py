@@ -229,6 +229,11 @@ def test_helpers_reject(lib):
     assert lib.nr_stream_copy(None, FAKE, 4, None) == 1
     assert lib.nr_stream_copy(FAKE, FAKE, 4, None) == 1
     assert lib.nr_stream_copy(FAKE + 1, FAKE + 64, 4, None) == 2
+    assert lib.nr_stream_copy_ws(None, FAKE, 4, FAKE, 256, None) == 1
+    assert lib.nr_stream_copy_ws(FAKE, FAKE + 8, 4, FAKE + 4096, 256, None) == 1   # overlap
+    assert lib.nr_stream_copy_ws(FAKE, FAKE + 4096, 4, None, 256, None) == 4        # no workspace
+    assert lib.nr_stream_copy_ws(FAKE, FAKE + 4096, 4, FAKE + 8192, 255, None) == 4  # too small
+    assert lib.nr_stream_copy_ws(FAKE, FAKE + 4096, 4, FAKE + 8200, 256, None) == 4  # misaligned
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1136,3 +1136,12 @@ def test_stream_copy(dev, nra):
     nra.stream_copy(c, d)
     torch.cuda.synchronize()
     assert torch.equal(c, d)
+    # the persistent copy: whole 64 KiB units, a ragged last unit, fewer units than CUs, and
+    # two calls in a row on one workspace (its counter is zeroed by every call)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    for n in (1 << 24, (1 << 22) + 4 * 37, 4096 * 3 + 8, 1001):
+        a = torch.randn(n, device=dev)
+        b = torch.full_like(a, float("nan"))
+        nra.stream_copy(a, b, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), n
