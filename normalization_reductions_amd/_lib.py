@@ -9,7 +9,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libnormred.so")
+# NORMRED_LIB selects another build of the same library (the host-sanitizer test loads its
+# AddressSanitizer build this way)
+LIB_PATH = os.environ.get("NORMRED_LIB") or os.path.join(PKG, "libnormred.so")
 
 NR_OK = 0
 NR_ERR_INVALID_ARG = 1

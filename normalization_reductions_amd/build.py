@@ -65,5 +65,34 @@ def build(debug: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+def build_host_asan(outdir: str) -> tuple[str, str]:
+    """Debug builds of the host code for the sanitizer test: abi.cpp (the C ABI's validation,
+    planning and dispatch) with g++ -O0 -g and AddressSanitizer + UndefinedBehaviorSanitizer,
+    linked with the device objects of the last build() into libnormred_asan.so, and oracle.c
+    the same way into liboracle_asan.so. Device code is not sanitized. Returns both paths."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    os.makedirs(outdir, exist_ok=True)
+    san = ["-O0", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined"]
+    abi_o = os.path.join(outdir, "abi_asan.o")
+    lib = os.path.join(outdir, "libnormred_asan.so")
+    orc = os.path.join(outdir, "liboracle_asan.so")
+    dev_objs = sorted(glob.glob(os.path.join(OBJDIR, "*.hip.o")))
+    if not dev_objs:
+        raise RuntimeError("no device objects in %s: run build() first" % OBJDIR)
+    steps = [
+        ["g++", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+         "-I", INCLUDE, "-I", CSRC] + san + ["-c", os.path.join(CSRC, "abi.cpp"), "-o", abi_o],
+        ["g++", "-shared", "-fsanitize=address,undefined", "-o", lib, abi_o] + dev_objs +
+        ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")],
+        ["gcc", "-std=c11", "-fPIC", "-shared", "-pthread"] + san +
+        ["-o", orc, os.path.join(ROOT, "oracle", "oracle.c"), "-lm"],
+    ]
+    for cmd in steps:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("sanitizer build failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    return lib, orc
+
+
 if __name__ == "__main__":
     print(build())

@@ -23,7 +23,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# NORMRED_ORACLE_LIB selects another build of oracle.c (the host-sanitizer test's)
+_LIB = os.environ.get("NORMRED_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
