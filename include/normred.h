@@ -180,8 +180,8 @@ nr_status bn_train_forward_ex(const float* x, float* y, int64_t N, int64_t C, in
  * partials of 16 bytes, J a few per batch item), so no pass re-reads the conv output for them.
  * Precision: the conv is fp32-accurate. On that 2-D shape its products come from exact
  * three-part bf16 splits of x and w (six partial products; each part left out is below
- * 2^-24 |x w|), and the statistics of channels of at least 16384 values use four partial
- * products (x in two parts), whose per-value error averages out of the mean and variance.
+ * 2^-24 |x w|); the statistics pass forms the same products as the pass that normalizes, so a
+ * channel of zero variance (e.g. a constant input) gives exactly beta * out_scale.
  *
  * Channels last (channels_last = 1; IN3d page, its note on an (N, spatial, C) layout that makes
  * the max over channels contiguous): x is [N, (D,) H, W, C_in] and out is
