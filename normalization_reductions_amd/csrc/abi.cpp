@@ -19,15 +19,21 @@ namespace {
 
 thread_local std::string t_err;
 
+nr_status vfail(nr_status s, const char* fmt, va_list ap)
+{
+    char buf[512];
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    t_err = buf;
+    return s;
+}
+
 nr_status fail(nr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 nr_status fail(nr_status s, const char* fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof(buf), fmt, ap);
+    vfail(s, fmt, ap);
     va_end(ap);
-    t_err = buf;
     return s;
 }
 
@@ -35,12 +41,10 @@ nr_status fail(nr_status s, const char* fmt, ...)
 
 nr_status nr::set_error(nr_status s, const char* fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof(buf), fmt, ap);
+    vfail(s, fmt, ap);
     va_end(ap);
-    t_err = buf;
     return s;
 }
 

@@ -1121,6 +1121,16 @@ def test_native_c_abi_roundtrip(dev, orc, tmp_path):
     z = np.fromfile(tmp_path / "bn.bin", np.float32).reshape(shape)
     assert maxerr(y, orc.instance_norm(x)) <= TOL
     assert maxerr(z, orc.batch_norm_train(x, scale=2.0)) <= TOL
+    u = np.fromfile(tmp_path / "noalloc.bin", np.float32).reshape(shape)
+    assert np.array_equal(u, y)  # the same kernels in the library's own workspace
+    x5 = np.fromfile(tmp_path / "x5.bin", np.float32).reshape(2, 3, 6, 9, 11)
+    w5 = np.fromfile(tmp_path / "w5.bin", np.float32).reshape(16, 3, 3, 3, 3)
+    b5 = np.fromfile(tmp_path / "b5.bin", np.float32)
+    m5 = np.fromfile(tmp_path / "m5.bin", np.float32)
+    out5 = np.fromfile(tmp_path / "chain.bin", np.float32).reshape(2, 4, 7, 9)
+    ref5 = orc.conv_norm_epilogue(x5, w5, b5, batch=False, pre_mul=m5, clamp=(-1.0, 1.0),
+                                  post_mul=m5, reduce_max_c=True)
+    assert maxerr(out5, ref5) <= TOL
 
 
 def test_stream_copy(dev, nra):
