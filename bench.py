@@ -194,7 +194,7 @@ def cpu_baseline(x, y, budget_s, torch):
     return ({"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
              "sample": "first %d of %d slices (%d x 262144 fp32), fp64 oracle, %.1f s wall"
                        % (m, N * C, m, dt),
-             "host": host_description()},
+             "wall_s": round(dt, 3), "host": host_description()},
             {"slices": m, "max_abs_err": err})
 
 
@@ -221,6 +221,113 @@ def copy_ceiling(torch, nra, x, y, steps, warmup):
     gbps = MIN_BYTES / (per / 1e3) / 1e9
     log("persistent copy of the same bytes (the ceiling): %.3f ms -> %.1f GB/s" % (per, gbps))
     return gbps
+
+
+CONFIGS = {
+    1: "InstanceNorm2d fp32, affine=False, eps=1e-5: x[2,4,32,32] ~ N(0,1)*s+o, per slice "
+       "s~U(0.5,2), o~U(-3,3)",
+    2: "InstanceNorm2d fp32, affine=False, eps=1e-5: x[16,64,256,256], per slice o~U(-100,100), "
+       "s~U(0.1,10) on N(0,1)",
+    3: "InstanceNorm2d fp32, affine=False, eps=1e-5: x[112,64,512,512] ~ N(0,1)",
+    4: "Conv2d(8->64,k=3,valid,bias) on x[128,8,64,64]~N(0,1); training-mode BatchNorm2d, "
+       "eps=1e-5; x2.0",
+    5: "Conv3d(3->16,k=3,valid,bias) on x[128,3,16,32,32]~N(0,1); x multiplier; InstanceNorm3d; "
+       "clamp[-1,1]; x multiplier; max over C",
+}
+
+
+def config_results(torch, nra, head, x3_sha, steps, warmup, out_dir):
+    """Part of the CPU-baseline leg: one JSON file per workload in out_dir, with its GPU time
+    (HIP events around each call; workloads 1, 2, 4, 5 after a 512 MB read that empties the
+    caches), the fp64 oracle's time on the host cores over the same inputs, and the maximum
+    |gpu - oracle| over every output element. Workload 3 reuses the headline's measurements."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    os.makedirs(out_dir, exist_ok=True)
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    flush = lambda: scrub.sum()
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+    def record(cfg, rec):
+        rec = dict({"config": cfg, "workload": CONFIGS[cfg], "tolerance_max_abs": 1e-4,
+                    "oracle": "fp64 CPU oracle (oracle/oracle.c), %d threads" % threads}, **rec)
+        with open(os.path.join(out_dir, "config%d.json" % cfg), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        log("config %d: %s" % (cfg, json.dumps({k: rec[k] for k in ("gpu_ms_median", "max_abs_err_vs_oracle")})))
+
+    def gpu_time(fn):
+        tot, mean, med = time_calls(fn, steps, warmup, torch, flush)
+        return {"gpu_ms_median": round(med, 5), "gpu_ms_mean": round(mean, 5),
+                "gpu_ms_min": round(time_calls.last[0], 5)}
+
+    for cfg in (1, 2):
+        inp = synth.host_inputs(cfg)
+        x = T(inp["x"])
+        y = torch.empty_like(x)
+        rec = gpu_time(lambda: nra.inorm_forward(x, y, eps=inp["eps"]))
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ref = oracle.instance_norm(inp["x"], eps=inp["eps"], nthreads=threads)
+        dt = time.perf_counter() - t
+        nbytes = 2 * 4 * x.numel()
+        rec.update({"shape": list(inp["x"].shape), "input_sha256": {"x": sha256_host(inp["x"])},
+                    "min_bytes": nbytes, "GBps": round(nbytes / (rec["gpu_ms_median"] / 1e3) / 1e9, 1),
+                    "oracle_s": round(dt, 3),
+                    "max_abs_err_vs_oracle": float(np.max(np.abs(y.cpu().numpy().astype(np.float64) - ref))),
+                    "elements_compared": int(x.numel())})
+        record(cfg, rec)
+        del x, y
+    record(3, {"shape": [N, C, H, W], "input_sha256": {"x": x3_sha}, "min_bytes": MIN_BYTES,
+               "gpu_ms_median": head["median"], "gpu_ms_mean": head["mean"], "gpu_ms_min": head["min"],
+               "GBps": round(MIN_BYTES / (head["median"] / 1e3) / 1e9, 1),
+               "timing": "HIP events around each call, inputs resident, no cache emptying (15 GB)",
+               "oracle_s": head["oracle_s"], "max_abs_err_vs_oracle": head["max_abs_err"],
+               "elements_compared": head["elements"]})
+    conv_gflop = {4: 2 * 128 * 64 * 62 * 62 * 72 / 1e9, 5: 2 * 128 * 16 * 12600 * 81 / 1e9}
+    for cfg in (4, 5):
+        inp = synth.host_inputs(cfg)
+        a = (T(inp["x"]), T(inp["w"]), T(inp["b"]))
+        if cfg == 4:
+            out = torch.empty((128, 64, 62, 62), device=dev)
+            g, be = T(inp["gamma"]), T(inp["beta"])
+            fn = lambda: nra.conv_norm_epilogue_forward(*a, out=out, norm=nra.NR_NORM_BATCH_TRAIN,
+                                                        eps=inp["eps"], gamma=g, beta=be,
+                                                        out_scale=inp["scale"])
+            orc = lambda: oracle.conv_norm_epilogue(inp["x"], inp["w"], inp["b"], batch=True,
+                                                    gamma=inp["gamma"], beta=inp["beta"],
+                                                    out_scale=inp["scale"], nthreads=threads)
+            keys = ("x", "w", "b", "gamma", "beta")
+        else:
+            out = torch.empty((128, 14, 30, 30), device=dev)
+            m = T(inp["mult"])
+            fn = lambda: nra.conv_norm_epilogue_forward(*a, out=out, norm=nra.NR_NORM_INSTANCE,
+                                                        eps=inp["eps"], pre_mul=m, clamp=inp["clamp"],
+                                                        post_mul=m, reduce_max_c=True)
+            orc = lambda: oracle.conv_norm_epilogue(inp["x"], inp["w"], inp["b"], batch=False,
+                                                    pre_mul=inp["mult"], clamp=inp["clamp"],
+                                                    post_mul=inp["mult"], reduce_max_c=True,
+                                                    nthreads=threads)
+            keys = ("x", "w", "b", "mult")
+        rec = gpu_time(fn)
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ref = orc()
+        dt = time.perf_counter() - t
+        rec.update({"shape": list(inp["x"].shape), "input_sha256": {k: sha256_host(inp[k]) for k in keys},
+                    "conv_gflop": round(conv_gflop[cfg], 3),
+                    "conv_TFLOPs_over_chain_time": round(conv_gflop[cfg] / rec["gpu_ms_median"], 2),
+                    "oracle_s": round(dt, 3),
+                    "max_abs_err_vs_oracle": float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))),
+                    "elements_compared": int(out.numel())})
+        record(cfg, rec)
+        del a, out
 
 
 def extras(torch, nra, x, y, steps, warmup):
@@ -402,6 +509,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--results-dir", default=None,
+                    help="with the CPU baseline: also write one JSON per workload (1-5) into this "
+                         "directory (GPU time, oracle time, max |gpu - oracle| over every output)")
     ap.add_argument("--conv-producers", action="store_true",
                     help="time the conv producers alone (vector ALU against matrix cores) on the "
                          "two model shapes, print one JSON line and exit")
@@ -493,6 +603,11 @@ def main() -> int:
         cb, par = cpu_baseline(x, y, args.cpu_seconds, torch)
         res["cpu_baseline"] = cb
         res["parity_sample"] = par
+        if args.results_dir:
+            head = {"median": round(launch_med, 5), "mean": round(launch_ms, 5),
+                    "min": round(launch_min, 5), "max_abs_err": par["max_abs_err"],
+                    "elements": par["slices"] * S, "oracle_s": cb["wall_s"]}
+            config_results(torch, nra, head, x_sha, args.steps, min(args.warmup, 3), args.results_dir)
     print(json.dumps(res), flush=True)
     return 0
 
