@@ -396,8 +396,8 @@ ChainLayout chain_layout(const ConvGeom& g, bool batch, bool reduce_max_c)
         const int64_t G = conv2d_c8_grid_bound(g);
         L.c8part = off;
         off = align_up(off + (size_t)(g.Cout * G) * sizeof(float4), kWsAlign);
-        L.c8stats = off;
-        off = align_up(off + (size_t)g.Cout * sizeof(GroupStat), kWsAlign);
+        L.c8stats = off;  // the published statistics: [C_out][2] tagged 64-bit words
+        off = align_up(off + (size_t)g.Cout * 2 * sizeof(unsigned long long), kWsAlign);
     }
     if (!reduce_max_c && g.SP % 4 == 0 && choose_resident(len, batch, true, &L.cfg_idx, &L.P) &&
         groups * L.P <= 0xF0000000LL && groups <= 0x7fffffffLL) {
@@ -659,6 +659,10 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         C8Chain c8;
         c8.pre_mul = d->pre_mul;
         c8.part = ws_at<float4>(workspace, L.c8part);
+        c8.xstats = ws_at<unsigned long long>(workspace, L.c8stats);
+        c8.eps = d->eps;
+        c8.run = RunningStats{d->running_mean, d->running_var, d->momentum};
+        c8.flags = ws_at<uint32_t>(workspace, 0);
         c8.gamma = d->gamma;
         c8.beta = d->beta;
         c8.out_scale = d->out_scale;
@@ -666,9 +670,7 @@ __attribute__((visibility("default"))) nr_status conv_norm_epilogue_forward(
         c8.lo = d->clamp_lo;
         c8.hi = d->clamp_hi;
         c8.post_mul = d->post_mul;
-        const hipError_t e = launch_conv2d_c8_bn_chain(
-            g, x, w, b, out, c8, ws_at<GroupStat>(workspace, L.c8stats), d->eps,
-            RunningStats{d->running_mean, d->running_var, d->momentum}, stream);
+        const hipError_t e = launch_conv2d_c8_bn_chain(g, x, w, b, out, c8, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }

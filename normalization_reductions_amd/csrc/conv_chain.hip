@@ -776,6 +776,39 @@ __device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsign
     l = bf16_rne(r1 - bf16_value(m));
 }
 
+constexpr uint32_t kC8Tag = 1u;  // the tag of a published word (cleared words carry 0)
+
+// The apply pass's merge of channel ch: the statistics pass's nparts partials of the channel,
+// thread-strided (thread t takes partials t, t + 256, ...), then a wave butterfly and the four
+// waves in order -- a fixed order. Thread 0 publishes the mean and 1/sqrt(biased var + eps) as
+// tagged words and blends the batch statistics into the running ones (BN page, opening
+// analysis: running = (1 - m) * running + m * batch, with the unbiased batch variance). Every
+// thread of the workgroup calls it; red holds 4 Stats of scratch.
+__device__ __forceinline__ void c8_merge_publish(const C8Chain& e, int ch, Stat* red)
+{
+    const float4* pp = e.part + (int64_t)ch * e.nparts;
+    Stat st = lane_strided_merge<256>(e.nparts, [&](int64_t i) {
+        const float4 p = pp[i];
+        return Stat{p.x, p.y, p.z};
+    });
+    st = wave_merge<kWave>(st);
+    if (lane_id() == 0) red[threadIdx.x / kWave] = st;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Stat t = red[0];
+        for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v]);
+        const float rstd = rsqrtf(t.m2 / t.n + e.eps);
+        xchg_store(e.xstats + 2 * ch, kC8Tag, t.mean);
+        xchg_store(e.xstats + 2 * ch + 1, kC8Tag, rstd);
+        if (e.run.mean) {
+            const float mo = e.run.momentum;
+            e.run.mean[ch] = (1.f - mo) * e.run.mean[ch] + mo * t.mean;
+            e.run.var[ch] = (1.f - mo) * e.run.var[ch] + mo * (t.m2 / (t.n - 1.f));
+        }
+    }
+    __syncthreads();
+}
+
 // Three modes share the producer: kC8Conv stores the conv output; kC8Stats stores nothing and
 // writes each workgroup's per-channel (count, mean, M2) of the values (conv + bias) * pre_mul,
 // for batch-norm statistics; kC8Apply recomputes the conv and stores the normalized chain
@@ -809,6 +842,15 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     const int OH = (int)g.OH;
     const int64_t HW = g.H * W;
     const int nbox = (OH + B - 1) / B;
+
+    // the statistics pass clears the words the apply pass publishes (stream order puts that
+    // before the apply pass); the apply pass's first workgroups merge and publish them
+    if (MODE == kC8Stats && blockIdx.x == 0)
+        for (int i = (int)threadIdx.x; i < 2 * kC8Cout; i += 256)
+            __hip_atomic_store(e.xstats + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (MODE == kC8Apply)
+        for (int ch = (int)blockIdx.x; ch < kC8Cout; ch += (int)gridDim.x)
+            c8_merge_publish(e, ch, reinterpret_cast<Stat*>(win));
 
     // B operands: lane l holds W[n][0..7][tap 2q + l/32] for n = 32 nt + l%32, in three splits.
     // The workgroup reads W once with coalesced loads, splits each value, and lays the splits
@@ -847,11 +889,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         pm1 = e.pre_mul[32 + m];
     }
     if (MODE == kC8Apply) {
-        const GroupStat s0 = e.stats[m], s1 = e.stats[32 + m];
-        mu0 = s0.pivot + s0.mean_d;
-        mu1 = s1.pivot + s1.mean_d;
-        A0 = s0.rstd * (e.gamma ? e.gamma[m] : 1.f) * e.out_scale;
-        A1 = s1.rstd * (e.gamma ? e.gamma[32 + m] : 1.f) * e.out_scale;
+        A0 = (e.gamma ? e.gamma[m] : 1.f) * e.out_scale;  // times rstd once it is published
+        A1 = (e.gamma ? e.gamma[32 + m] : 1.f) * e.out_scale;
         B0 = (e.beta ? e.beta[m] : 0.f) * e.out_scale;
         B1 = (e.beta ? e.beta[32 + m] : 0.f) * e.out_scale;
         if (e.post_mul) {
@@ -859,6 +898,33 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             q1 = e.post_mul[32 + m];
         }
     }
+    // The channel statistics, read before the first epilogue (after the first tile's matrix
+    // work, which hides the merge): a bounded wait for the four tagged words of channels m and
+    // 32 + m; if it gives up it raises the sticky flag (the results are then invalid).
+    bool have_stats = MODE != kC8Apply;
+    auto fetch_stats = [&]() {
+        unsigned long long w0, w1, w2, w3;
+        uint32_t spins = 0;
+        for (;;) {
+            w0 = xchg_load(e.xstats + 2 * m);
+            w1 = xchg_load(e.xstats + 2 * m + 1);
+            w2 = xchg_load(e.xstats + 2 * (32 + m));
+            w3 = xchg_load(e.xstats + 2 * (32 + m) + 1);
+            if ((uint32_t)(w0 >> 32) == e.wait_tag && (uint32_t)(w1 >> 32) == e.wait_tag &&
+                (uint32_t)(w2 >> 32) == e.wait_tag && (uint32_t)(w3 >> 32) == e.wait_tag)
+                break;
+            if (++spins > e.spin_limit) {
+                raise_flag(e.flags, kFlagSpinTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        mu0 = __uint_as_float((uint32_t)w0);
+        A0 *= __uint_as_float((uint32_t)w1);
+        mu1 = __uint_as_float((uint32_t)w2);
+        A1 *= __uint_as_float((uint32_t)w3);
+        have_stats = true;
+    };
     Stat run0 = stat_empty(), run1 = stat_empty();
 
     const int64_t total = g.N * (int64_t)nbox;
@@ -1008,6 +1074,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                     run1 = chan_merge(run1, Stat{fn, K1 + md1, d1});
                 }
             } else {
+                if (!have_stats) fetch_stats();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int p0 = ts + 8 * j + 4 * kk;  // positions of registers 4j..4j+3
@@ -1059,31 +1126,6 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + ch]);
             const float bc = b ? b[ch] : 0.f, pc = e.pre_mul ? e.pre_mul[ch] : 1.f;
             e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, mul_rn(t.mean + bc, pc), t.m2 * pc * pc, 0.f};
-        }
-    }
-}
-
-// Per-channel merge of the statistics pass's workgroup partials ([channel][workgroup]), one wave
-// per channel, in a fixed order (lanes stride the partials, then the fixed shuffle tree): the
-// channel's mean and 1/sqrt(biased var + eps), and the optional outputs of the batch-norm
-// entry points (saved statistics, running statistics with the unbiased variance).
-__global__ __launch_bounds__(kWave) void c8_stats_merge_kernel(const float4* __restrict__ part, int G,
-                                                                float eps, GroupStat* stats,
-                                                                RunningStats run)
-{
-    const int ch = blockIdx.x;
-    Stat st = lane_strided_merge<kWave>(G, [&](int64_t i) {
-        const float4 p = part[(int64_t)ch * G + i];
-        return Stat{p.x, p.y, p.z};
-    });
-    st = wave_merge<kWave>(st);
-    if (threadIdx.x == 0) {
-        const float rstd = rsqrtf(st.m2 / st.n + eps);
-        stats[ch] = GroupStat{0.f, st.mean, rstd, 0.f};
-        if (run.mean) {
-            const float mo = run.momentum;
-            run.mean[ch] = (1.f - mo) * run.mean[ch] + mo * st.mean;
-            run.var[ch] = (1.f - mo) * run.var[ch] + mo * (st.m2 / (st.n - 1.f));
         }
     }
 }
@@ -1416,17 +1458,24 @@ bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out)
            (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
 }
 
+// Two launches of the same grid: the statistics pass (partials per workgroup and channel; its
+// workgroup 0 clears the words the merge publishes), then the apply pass, whose first
+// workgroups merge one channel each before their own work. The apply pass's workgroups wait
+// only on workgroups that start before them (the lowest-numbered), which therefore run.
 hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
-                                     const float* b, float* out, C8Chain e, GroupStat* stats,
-                                     float eps, RunningStats run, hipStream_t stream)
+                                     const float* b, float* out, C8Chain e, hipStream_t stream)
 {
     const int64_t G = c8_grid(g);
+    e.nparts = (int)G;
+    // NORMRED_TEST_WAIT_GIVEUP=1 (tests of the failure path only), as for the read-once kernels:
+    // the wait looks for a tag nothing publishes and gives up after 64 polls
+    const char* giveup = getenv("NORMRED_TEST_WAIT_GIVEUP");
+    const bool test_giveup = giveup && giveup[0] == '1';
+    e.wait_tag = test_giveup ? kC8Tag + 1u : kC8Tag;
+    e.spin_limit = test_giveup ? 64u : kSpinLimit;
     conv2d_c8_bf16x6_kernel<kC8B, kC8Stats><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    c8_stats_merge_kernel<<<dim3((unsigned)g.Cout), dim3(kWave), 0, stream>>>(e.part, (int)G, eps, stats, run);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    e.stats = stats;
     conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
     return hipGetLastError();
 }

@@ -116,8 +116,17 @@ struct RingStats {
 // a batch-norm chain by recomputation (statistics pass, merge, apply pass).
 struct C8Chain {
     const float* pre_mul = nullptr;
-    float4* part = nullptr;         // statistics pass: [C_out][workgroups] (count, mean, M2, -)
-    const GroupStat* stats = nullptr;  // apply pass: per channel
+    float4* part = nullptr;         // [C_out][nparts] (count, mean, M2, -), by the statistics pass
+    // [C_out][2] tagged words (mean, rstd): zeroed by the statistics pass; the apply pass's
+    // first workgroups merge the partials of one channel each and publish them here, and every
+    // workgroup reads its channels' words before its first epilogue
+    unsigned long long* xstats = nullptr;
+    int nparts = 0;                 // partials per channel (the statistics pass's workgroups)
+    float eps = 0.f;
+    RunningStats run;               // optional running-statistics update (by the merging workgroups)
+    uint32_t* flags = nullptr;      // sticky error word: a wait for the published words gave up
+    uint32_t wait_tag = 1, spin_limit = 0;  // the tag the readers accept and their polling bound:
+                                            // set by the launcher (see launch_resident)
     const float* gamma = nullptr;
     const float* beta = nullptr;
     float out_scale = 1.f;
@@ -142,8 +151,7 @@ bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out);
 // stats (and the running statistics), then the conv again with the chain epilogue into out.
 // Needs conv2d_c8_shape(g) and 16-byte aligned x and out.
 hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
-                                     const float* b, float* out, C8Chain e, GroupStat* stats,
-                                     float eps, RunningStats run, hipStream_t stream);
+                                     const float* b, float* out, C8Chain e, hipStream_t stream);
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
                           float* c, hipStream_t stream);
 // Slots per batch item of the ring producer's own statistics for this shape, for any pointer

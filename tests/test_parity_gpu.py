@@ -235,7 +235,8 @@ def test_inorm_workspace_carries_no_state(dev, nra, orc):
 
 
 def test_exchange_wait_gives_up_and_raises_flag(dev, nra, orc, monkeypatch):
-    """The failure path of the read-once kernels' bounded exchange wait, forced from the host:
+    """The failure path of the bounded waits (the read-once kernels' exchange, and the
+    recomputing batch-norm chain's wait for its published statistics), forced from the host:
     under NORMRED_TEST_WAIT_GIVEUP=1 every wait looks for a tag no part publishes and gives up
     after 64 polls. The call must still finish (every kernel exits normally) and raise the
     sticky timeout flag, which nr_workspace_check reports once and clears; the next call
@@ -256,13 +257,35 @@ def test_exchange_wait_gives_up_and_raises_flag(dev, nra, orc, monkeypatch):
     nra.bn_train_forward(xbt, workspace=ws)
     torch.cuda.synchronize()
     assert nra.workspace_check(ws) & 1
+    # the recomputing Conv2d -> batch norm chain: its apply pass waits for the statistics its
+    # first workgroups publish
+    xc = g.standard_normal((4, 8, 18, 64)).astype(np.float32)
+    wc = (g.standard_normal((64, 8, 3, 3)) * 0.2).astype(np.float32)
+    bc = g.standard_normal(64).astype(np.float32)
+    rm, rv = T(np.zeros(64, np.float32), dev), T(np.ones(64, np.float32), dev)
+    cargs = (T(xc, dev), T(wc, dev), T(bc, dev))
+    wsc = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    nra.conv_norm_epilogue_forward(*cargs, norm=nra.NR_NORM_BATCH_TRAIN, workspace=wsc)
+    torch.cuda.synchronize()
+    assert nra.workspace_check(wsc) & 1
     monkeypatch.delenv("NORMRED_TEST_WAIT_GIVEUP")
     y = nra.inorm_forward(xt, workspace=ws)
     yb = nra.bn_train_forward(xbt, workspace=ws)
+    yc = nra.conv_norm_epilogue_forward(*cargs, norm=nra.NR_NORM_BATCH_TRAIN, running_mean=rm,
+                                        running_var=rv, momentum=0.5, workspace=wsc)
     torch.cuda.synchronize()
     assert nra.workspace_check(ws) == 0
+    assert nra.workspace_check(wsc) == 0
     assert maxerr(H(y), orc.instance_norm(x)) <= TOL
     assert maxerr(H(yb), orc.batch_norm_train(xb)) <= TOL
+    assert maxerr(H(yc), orc.conv_norm_epilogue(xc, wc, bc, batch=True)) <= TOL
+    c = orc.conv_k3(xc, wc, bc)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    n = c.size // 64
+    rm_ref, rv_ref = orc.bn_running_update(mean, var, n, np.zeros(64, np.float32),
+                                           np.ones(64, np.float32), momentum=0.5)
+    np.testing.assert_allclose(H(rm), rm_ref, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(H(rv), rv_ref, rtol=1e-5, atol=1e-6)
 
 
 def test_inorm_two_streams_concurrently(dev, nra, orc):
