@@ -192,3 +192,50 @@ def test_inorm_quantized(dev, nra, orc, shape):
     err = maxerr(H(y), orc.instance_norm(x))
     _log("inorm quantized %s: max_abs_err %.3e" % (shape, err))
     assert err <= TOL
+
+
+# Other plans of the conv chains with a constant input: the conv writes c into `out` and a
+# read-once kernel normalizes it in place (instance and batch groups, pipelined or one
+# workgroup), the split statistics path, the vector-ALU producer's shapes, channels last.
+PLAN_CASES = [
+    # (x shape, C_out, batch, reduce_max_c, channels_last)
+    ((1, 2, 260, 260), 3, False, False, False),   # in place, pipelined instance groups
+    ((40, 2, 42, 42), 4, True, False, False),     # in place, pipelined batch groups
+    ((9, 2, 40, 42), 6, True, False, False),      # in place, one workgroup per channel
+    ((2, 8, 15, 13), 64, True, False, False),     # split path (143 positions)
+    ((2, 3, 9, 11), 5, False, True, False),       # max over channels, statistics pass over c
+    ((3, 1, 5, 6, 7), 20, True, True, False),     # 3-D, batch norm, max over channels
+    ((3, 2, 9, 10), 4, True, False, True),        # channels last, batch norm, in place
+    ((2, 3, 6, 9, 11), 16, False, False, True),   # channels last, 3-D, ring statistics
+]
+
+
+@pytest.mark.parametrize("shape,cout,batch,red,cl", PLAN_CASES)
+@pytest.mark.parametrize("value", [0.7, -9.5])
+def test_conv_chain_plans_constant_input(dev, nra, orc, shape, cout, batch, red, cl, value):
+    g = np.random.Generator(np.random.PCG64(0x5EED050A + cout))
+    dims = len(shape) - 2
+    x = np.full(shape, np.float32(value), dtype=np.float32)
+    w = (g.standard_normal((cout, shape[1]) + (3,) * dims) * 0.3).astype(np.float32)
+    b = g.standard_normal(cout).astype(np.float32)
+    pm = g.uniform(0.5, 2.0, cout).astype(np.float32) * np.where(g.random(cout) < 0.5, -1, 1).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, cout).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, cout).astype(np.float32)
+    qm = g.standard_normal(cout).astype(np.float32)
+    _log("case chain plan %s Cout %d batch %s max_c %s cl %s value %s" % (shape, cout, batch, red, cl, value))
+    xin = _to_cl(x) if cl else x
+    out = nra.conv_norm_epilogue_forward(
+        T(xin, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN if batch else nra.NR_NORM_INSTANCE,
+        pre_mul=T(pm, dev), gamma=T(gm, dev), beta=T(bt, dev), out_scale=1.5, clamp=(-0.8, 1.1),
+        post_mul=T(qm, dev), reduce_max_c=red, channels_last=cl)
+    got = H(out) if (red or not cl) else np.moveaxis(H(out), -1, 1)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=batch, pre_mul=pm, gamma=gm, beta=bt, out_scale=1.5,
+                                 clamp=(-0.8, 1.1), post_mul=qm, reduce_max_c=red)
+    err = maxerr(got, ref)
+    _log("chain plan %s value %s: max_abs_err %.3e" % (shape, value, err))
+    assert err <= TOL
+    # the closed form: every channel is constant, so the normalized value is 0 and each output
+    # is clamp(beta * 1.5) * post_mul (max over the channels of that with the max)
+    z = np.clip(bt * np.float32(1.5), -0.8, 1.1) * qm
+    expect = np.max(z) if red else z.reshape((1, cout) + (1,) * dims)
+    assert maxerr(got, np.broadcast_to(expect, got.shape)) <= 1e-6
