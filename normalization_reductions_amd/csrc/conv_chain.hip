@@ -777,6 +777,19 @@ __device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsign
     l = bf16_rne(r1 - bf16_value(m));
 }
 
+// split3 of two values at once, each part packed as a pair (a in the low half): the hardware's
+// packed conversion rounds to nearest even, so the parts are split3's, bit for bit
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float mf2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3x2(float a, float b, unsigned& h, unsigned& m, unsigned& l)
+{
+    h = __builtin_bit_cast(unsigned, __builtin_convertvector(mf2{a, b}, bf2));
+    const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xFFFF0000u);
+    m = __builtin_bit_cast(unsigned, __builtin_convertvector(mf2{ra, rb}, bf2));
+    const float la = ra - __uint_as_float(m << 16), lb = rb - __uint_as_float(m & 0xFFFF0000u);
+    l = __builtin_bit_cast(unsigned, __builtin_convertvector(mf2{la, lb}, bf2));
+}
+
 constexpr uint32_t kC8Tag = 1u;  // the tag of a published word (cleared words carry 0)
 
 // The apply pass's merge of channel ch: the statistics pass's nparts partials of the channel,
@@ -926,7 +939,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         A1 *= __uint_as_float((uint32_t)w3);
         have_stats = true;
     };
-    Stat run0 = stat_empty(), run1 = stat_empty();
+    float K0 = 0.f, K1 = 0.f, cnt = 0.f, sum0 = 0.f, sum1 = 0.f, sq0 = 0.f, sq1 = 0.f;
 
     const int64_t total = g.N * (int64_t)nbox;
     const int64_t begin = total * blockIdx.x / gridDim.x;
@@ -950,13 +963,13 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         if (it < ITEMS) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                unsigned h[4], mm[4], lo[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) split3(pf[i][e], h[i], mm[i], lo[i]);
+                unsigned h01, m01, l01, h23, m23, l23;
+                split3x2(pf[0][e], pf[1][e], h01, m01, l01);
+                split3x2(pf[2][e], pf[3][e], h23, m23, l23);
                 unsigned short* d = win + buf * WIN + (srow * W + 4 * sj + e) * kC8Cin + 4 * scq;
-                *reinterpret_cast<mu2*>(d) = mu2{h[0] | h[1] << 16, h[2] | h[3] << 16};
-                *reinterpret_cast<mu2*>(d + SPLIT) = mu2{mm[0] | mm[1] << 16, mm[2] | mm[3] << 16};
-                *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
+                *reinterpret_cast<mu2*>(d) = mu2{h01, h23};
+                *reinterpret_cast<mu2*>(d + SPLIT) = mu2{m01, m23};
+                *reinterpret_cast<mu2*>(d + 2 * SPLIT) = mu2{l01, l23};
             }
         }
     };
@@ -1018,62 +1031,47 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             }
             if (MODE == kC8Stats) {
                 // positions this tile owns: from 32 t on for a tile t < tiles (an overlapping
-                // last tile starts earlier), none for a repeated tile
+                // last tile starts earlier), none for a repeated tile. A lane's registers hold
+                // positions ts + 8 (r / 4) + 4 kk + r % 4, increasing with r, so it owns the
+                // registers from r0 on. Each lane sums the raw conv sums shifted by its pivot
+                // (its first value of a tile with owned values, so a constant channel sums exact
+                // zeros and keeps the pivot as its mean): per tile, then into the lane's totals. The bias and
+                // pre-multiplier enter once per workgroup (mean (m + b) * pm, M2 * pm^2) when the
+                // partial is written, rounded as the apply pass rounds each value.
                 const int t = wave + 4 * i;
                 const int own = t < tiles ? 32 * t : BP;
-                // statistics of the raw sums, shifted by the lane's first owned value (so a
-                // constant channel gives exactly that value as its mean); the bias and
-                // pre-multiplier enter once per workgroup (mean (m + b) * pm, M2 * pm^2) when
-                // the partial is written, rounded as the apply pass rounds each value
-                const mf16& v0 = acc0;
-                const mf16& v1 = acc1;
-                if (ts == own) {  // the whole tile is owned (all but a box's last or repeated tiles)
-                    const float K0 = v0[0], K1 = v1[0];
-                    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s0 += v0[r] - K0;
-                        s1 += v1[r] - K1;
-                    }
-                    const float md0 = s0 * 0.0625f, md1 = s1 * 0.0625f;
-                    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        d0 = fmaf(v0[r] - K0 - md0, v0[r] - K0 - md0, d0);
-                        d1 = fmaf(v1[r] - K1 - md1, v1[r] - K1 - md1, d1);
-                    }
-                    run0 = chan_merge(run0, Stat{16.f, K0 + md0, d0});
-                    run1 = chan_merge(run1, Stat{16.f, K1 + md1, d1});
-                    continue;
+                if (cnt == 0.f) {  // nothing summed yet: (re)take the pivot
+                    K0 = acc0[0];
+                    K1 = acc1[0];
                 }
-                int cnt = 0;
-                float K0 = 0.f, K1 = 0.f;
-#pragma unroll
-                for (int r = 15; r >= 0; --r) {
-                    const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
-                    cnt += in;
-                    K0 = in ? v0[r] : K0;
-                    K1 = in ? v1[r] : K1;
-                }
-                if (cnt > 0) {
-                    float s0 = 0.f, s1 = 0.f;
+                acc0 -= K0;
+                acc1 -= K1;
+                if (ts < own) {  // a box's overlapping last tile or a repeated tile
+                    // not-owned registers: 4 for each whole 8 positions before own, then the
+                    // rest of that group of 4
+                    const int lead = max(0, own - ts - 4 * kk);
+                    const int r0 = min(16, 4 * (lead >> 3) + min(4, lead & 7));
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
-                        s0 += in ? v0[r] - K0 : 0.f;
-                        s1 += in ? v1[r] - K1 : 0.f;
+                        acc0[r] = r >= r0 ? acc0[r] : 0.f;
+                        acc1[r] = r >= r0 ? acc1[r] : 0.f;
                     }
-                    const float fn = (float)cnt, md0 = s0 / fn, md1 = s1 / fn;
-                    float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const bool in = ts + 8 * (r >> 2) + 4 * kk + (r & 3) >= own;
-                        d0 = in ? fmaf(v0[r] - K0 - md0, v0[r] - K0 - md0, d0) : d0;
-                        d1 = in ? fmaf(v1[r] - K1 - md1, v1[r] - K1 - md1, d1) : d1;
-                    }
-                    run0 = chan_merge(run0, Stat{fn, K0 + md0, d0});
-                    run1 = chan_merge(run1, Stat{fn, K1 + md1, d1});
+                    cnt += (float)(16 - r0);
+                } else {
+                    cnt += 16.f;
                 }
+                float s0 = 0.f, s1 = 0.f, d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s0 += acc0[r];
+                    s1 += acc1[r];
+                    d0 = fmaf(acc0[r], acc0[r], d0);
+                    d1 = fmaf(acc1[r], acc1[r], d1);
+                }
+                sum0 += s0;
+                sum1 += s1;
+                sq0 += d0;
+                sq1 += d1;
             } else {
                 if (!have_stats) fetch_stats();
 #pragma unroll
@@ -1104,7 +1102,15 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         buf ^= 1;
     }
     if (MODE == kC8Stats) {
-        // lane halves hold the same channels (lower half first), then the waves in order
+        // the lane's statistics from its shifted sums, then the lane halves (they hold the same
+        // channels; lower half first), then the waves in order
+        Stat run0 = stat_empty(), run1 = stat_empty();
+        if (cnt > 0.f) {
+            const float rn = __builtin_amdgcn_rcpf(cnt), md0 = sum0 * rn, md1 = sum1 * rn;
+            const float v0 = sq0 - sum0 * md0, v1 = sq1 - sum1 * md1;  // >= 0 but for rounding
+            run0 = Stat{cnt, K0 + md0, v0 < 0.f ? 0.f : v0};
+            run1 = Stat{cnt, K1 + md1, v1 < 0.f ? 0.f : v1};
+        }
         Stat o0, o1;
         o0.n = __shfl_xor(run0.n, 32);
         o0.mean = __shfl_xor(run0.mean, 32);
