@@ -851,11 +851,36 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     static_assert(ITEMS <= 256, "one staging item per thread");
     constexpr int TPW = ((B * OW + 31) / 32 + 3) / 4;  // tiles of 32 positions per wave and box
     __shared__ __attribute__((aligned(16))) unsigned short win[2 * WIN > WSTAGE ? 2 * WIN : WSTAGE];
+    // per-wave transpose of an output tile before its stores: 32 channels x 32 positions, rows
+    // padded to 36 floats (144 bytes) so both the column writes and the row reads of 16 bytes
+    // spread over the banks
+    constexpr int TR = 36;
+    __shared__ __attribute__((aligned(16))) float tr[MODE == kC8Stats ? 4 : 4 * 32 * TR];
     const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = l & 31, kk = l >> 5;
     const int OH = (int)g.OH;
     const int64_t HW = g.H * W;
     const int nbox = (OH + B - 1) / B;
+
+    const int64_t total = g.N * (int64_t)nbox;
+    const int64_t begin = total * blockIdx.x / gridDim.x;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    // staging item of this thread: window row, 4 columns, 4 channels (consecutive threads take
+    // consecutive columns, so each channel's loads are coalesced)
+    const int it = threadIdx.x;
+    const int srow = it >> 5, scq = (it >> 4) & 1, sj = it & 15;
+    mf4 pf[4] = {};
+    auto fetch = [&](int64_t box) {
+        const int64_t n = box / nbox;
+        const int o0 = (int)(box - n * nbox) * B;
+        const int rows = min(B, OH - o0) + 2;  // rows past the box's need are not loaded
+        if (it < ITEMS && srow < rows) {
+            const float* xs = x + (n * kC8Cin + 4 * scq) * HW + (int64_t)(o0 + srow) * W + 4 * sj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const mf4*>(xs + i * HW);
+        }
+    };
+    if (begin < end) fetch(begin);  // the first window's loads overlap the W staging
 
     // the statistics pass clears the words the apply pass publishes (stream order puts that
     // before the apply pass); the apply pass's first workgroups merge and publish them
@@ -941,24 +966,6 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     };
     float K0 = 0.f, K1 = 0.f, cnt = 0.f, sum0 = 0.f, sum1 = 0.f, sq0 = 0.f, sq1 = 0.f;
 
-    const int64_t total = g.N * (int64_t)nbox;
-    const int64_t begin = total * blockIdx.x / gridDim.x;
-    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
-    // staging item of this thread: window row, 4 columns, 4 channels (consecutive threads take
-    // consecutive columns, so each channel's loads are coalesced)
-    const int it = threadIdx.x;
-    const int srow = it >> 5, scq = (it >> 4) & 1, sj = it & 15;
-    mf4 pf[4] = {};
-    auto fetch = [&](int64_t box) {
-        const int64_t n = box / nbox;
-        const int o0 = (int)(box - n * nbox) * B;
-        const int rows = min(B, OH - o0) + 2;  // rows past the box's need are not loaded
-        if (it < ITEMS && srow < rows) {
-            const float* xs = x + (n * kC8Cin + 4 * scq) * HW + (int64_t)(o0 + srow) * W + 4 * sj;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const mf4*>(xs + i * HW);
-        }
-    };
     auto drop = [&](int buf) {
         if (it < ITEMS) {
 #pragma unroll
@@ -979,7 +986,6 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             e.part[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = float4{0.f, 0.f, 0.f, 0.f};
         return;
     }
-    fetch(begin);
     drop(0);
     __syncthreads();
     int buf = 0;
@@ -990,8 +996,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int64_t n = box / nbox;
         const int o0 = (int)(box - n * nbox) * B;
         const int BP = min(B, OH - o0) * OW;  // positions in this box: a multiple of 4, >= 62
-        float* c0 = MODE == kC8Stats ? nullptr : c + (n * kC8Cout + m) * g.SP + (int64_t)o0 * OW;
-        float* c1 = MODE == kC8Stats ? nullptr : c0 + 32 * g.SP;
+        // lane l stores 16 bytes of channel l / 8 + 8 s at position 4 (l % 8) of a tile
+        float* cb = MODE == kC8Stats ? nullptr : c + (n * kC8Cout + (l >> 3)) * g.SP + (int64_t)o0 * OW + 4 * (l & 7);
         // exactly TPW tiles per wave, each 32 whole positions of the box: the last tile ends at
         // the box's last position (overlapping the one before), and waves with no tile left
         // repeat the last. Overlaps rewrite bitwise-identical values, and every lane issues the
@@ -1009,6 +1015,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             const unsigned short* a1 = a0 + kk * kC8Cin;
             const unsigned short* a2 = a0 + kk * (W - 2) * kC8Cin;
             mf16 acc0 = {}, acc1 = {};
+            // the statistics pass gains from the scheduler's interleave of LDS reads and matrix
+            // instructions (-6 %); the storing passes do not
+            if (MODE == kC8Stats) __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
             for (int q = 0; q < kBfChunks; ++q) {
                 const int off = (q == 0 ? 0 : q == 1 ? 2 : q == 2 ? W + 1 : q == 3 ? 2 * W : 2 * W + 2) * kC8Cin;
@@ -1074,26 +1083,36 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 sq1 += d1;
             } else {
                 if (!have_stats) fetch_stats();
+                // the lane's values are channel m (acc0) or 32 + m (acc1) at positions
+                // ts + 8 j + 4 kk + 0..3; the epilogue runs on them as they are, then the wave
+                // transposes each 32 x 32 tile through its LDS rows so that 8 consecutive lanes
+                // store 128 contiguous bytes of one channel
+                float* trw = tr + wave * 32 * TR;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p0 = ts + 8 * j + 4 * kk;  // positions of registers 4j..4j+3
-                    mf4 z0 = mf4{acc0[4 * j], acc0[4 * j + 1], acc0[4 * j + 2], acc0[4 * j + 3]} + bias0;
-                    mf4 z1 = mf4{acc1[4 * j], acc1[4 * j + 1], acc1[4 * j + 2], acc1[4 * j + 3]} + bias1;
-                    if (MODE == kC8Apply) {
-                        z0 = (mul_rn(z0, pm0) - mu0) * A0 + B0;
-                        z1 = (mul_rn(z1, pm1) - mu1) * A1 + B1;
-                        if (e.clamp) {
+                for (int h = 0; h < 2; ++h) {
+                    const mf16& acc = h ? acc1 : acc0;
+                    const float bias = h ? bias1 : bias0, pm = h ? pm1 : pm0, mu = h ? mu1 : mu0;
+                    const float A = h ? A1 : A0, Bc = h ? B1 : B0, qm = h ? q1 : q0;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                z0[r] = fminf(fmaxf(z0[r], e.lo), e.hi);
-                                z1[r] = fminf(fmaxf(z1[r], e.lo), e.hi);
+                    for (int j = 0; j < 4; ++j) {
+                        mf4 z = mf4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]} + bias;
+                        if (MODE == kC8Apply) {
+                            z = (mul_rn(z, pm) - mu) * A + Bc;
+                            if (e.clamp) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) z[r] = fminf(fmaxf(z[r], e.lo), e.hi);
                             }
+                            z *= qm;
                         }
-                        z0 *= q0;
-                        z1 *= q1;
+                        *reinterpret_cast<mf4*>(trw + m * TR + 8 * j + 4 * kk) = z;
                     }
-                    *reinterpret_cast<mf4*>(c0 + p0) = z0;
-                    *reinterpret_cast<mf4*>(c1 + p0) = z1;
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const mf4 z = *reinterpret_cast<const mf4*>(trw + ((l >> 3) + 8 * s) * TR + 4 * (l & 7));
+                        *reinterpret_cast<mf4*>(cb + (int64_t)(32 * h + 8 * s) * g.SP + ts) = z;
+                    }
+                    __builtin_amdgcn_wave_barrier();
                 }
             }
         }
