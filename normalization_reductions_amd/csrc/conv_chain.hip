@@ -880,7 +880,6 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const mf4*>(xs + i * HW);
         }
     };
-    if (begin < end) fetch(begin);  // the first window's loads overlap the W staging
 
     // the statistics pass clears the words the apply pass publishes (stream order puts that
     // before the apply pass); the apply pass's first workgroups merge and publish them
@@ -890,6 +889,15 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     if (MODE == kC8Apply)
         for (int ch = (int)blockIdx.x; ch < kC8Cout; ch += (int)gridDim.x)
             c8_merge_publish(e, ch, reinterpret_cast<Stat*>(win));
+
+    // all of a thread's W loads are issued at once, then the first window's: the loads complete
+    // in order, so the W staging waits for W alone while the window's loads are in flight
+    constexpr int WPT = kC8Cout * kC8K / 256;
+    static_assert(kC8Cout * kC8K % 256 == 0, "W values split evenly over the threads");
+    float wv[WPT];
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) wv[k] = w[(int)threadIdx.x + 256 * k];
+    if (begin < end) fetch(begin);
 
     // B operands: lane l holds W[n][0..7][tap 2q + l/32] for n = 32 nt + l%32, in three splits.
     // The workgroup reads W once with coalesced loads, splits each value, and lays the splits
@@ -901,10 +909,12 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int nt = i / 96, sp = (i / 32) % 3, lane = 32 + i % 32;
         *reinterpret_cast<mu4*>(win + (((nt * kBfChunks + kBfChunks - 1) * 3 + sp) * 64 + lane) * 8) = mu4{0, 0, 0, 0};
     }
-    for (int i = (int)threadIdx.x; i < kC8Cout * kC8K; i += 256) {
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+        const int i = (int)threadIdx.x + 256 * k;
         const int n = i / kC8K, rem = i - n * kC8K, ci = rem / 9, tap = rem - ci * 9;
         unsigned h, mm, lo;
-        split3(w[i], h, mm, lo);
+        split3(wv[k], h, mm, lo);
         unsigned short* d = win + (((n >> 5) * kBfChunks + (tap >> 1)) * 3 * 64 + (n & 31) + 32 * (tap & 1)) * 8 + ci;
         d[0] = (unsigned short)h;
         d[64 * 8] = (unsigned short)mm;
