@@ -387,31 +387,35 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         const int ci = i / rg.inner_in;
         src[e] = i >= slice_floats ? -1 : CL ? i : (int)(ci * cstride) + (i - ci * rg.inner_in);
     }
-    mf4 pf[PF];
+    mf4 pf[PF];       // the next slice, loaded one step ahead
+    mf4 rw[3][PF];    // the first run's window: its three slices, loaded together
     // Load input slice j of batch item n (all channels) into registers / store it into its slot.
-    auto fetch = [&](int64_t n, int j) {
+    auto fetch = [&](mf4(&d)[PF], int64_t n, int j) {
         const float* xs = CL ? x + (n * rg.outer_in + j) * (int64_t)slice_floats
                              : x + n * Cin * cstride + (int64_t)j * rg.inner_in;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             if (src[e] < 0) continue;
             if (VEC)
-                pf[e] = *reinterpret_cast<const mf4*>(xs + src[e]);
+                d[e] = *reinterpret_cast<const mf4*>(xs + src[e]);
             else
-                pf[e >> 2][e & 3] = xs[src[e]];
+                d[e >> 2][e & 3] = xs[src[e]];
         }
     };
-    auto drop = [&](int j) {
+    auto drop = [&](const mf4(&d)[PF], int j) {
         float* dst = ring + (j & 3) * slice_floats + (int)threadIdx.x * (VEC ? 4 : 1);
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             if (src[e] < 0) continue;
             if (VEC)
-                *reinterpret_cast<mf4*>(dst + 4 * e * kMfmaBlock) = pf[e];
+                *reinterpret_cast<mf4*>(dst + 4 * e * kMfmaBlock) = d[e];
             else
-                dst[e * kMfmaBlock] = pf[e >> 2][e & 3];
+                dst[e * kMfmaBlock] = d[e >> 2][e & 3];
         }
     };
+    const int64_t total = (int64_t)g.N * rg.OO * rg.T;
+    const int64_t begin = total * blockIdx.x / gridDim.x;
+    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
 
     // This lane's B fragment (channel ch, taps 4s + q): weight, outer tap a (kd in 3-D, kh in
     // 2-D) and the offset of the tap inside one slot, packed as (a << 24) | offset. W is read
@@ -420,10 +424,34 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
     // line per lane and load, and registers still awaiting a global load at the step loop make
     // the compiler wait for all loads in flight -- the next slice's prefetch included -- before
     // the tile loop.
+    // The W loads are issued together, then the first run's window (its loads complete in order
+    // behind W's, so the W staging waits for W alone); a loop that waited on each load in turn
+    // and a window staged slice by slice put one memory latency per value or slice before the
+    // first step.
     const int ch = wn * 16 + r16;
     const int wcount = (int)g.Cout * K;  // the launcher sizes the ring to hold W and the bias
-    for (int i = (int)threadIdx.x; i < wcount; i += kMfmaBlock) ring[i] = w[i];
-    for (int i = (int)threadIdx.x; i < (int)g.Cout; i += kMfmaBlock) ring[wcount + i] = b ? b[i] : 0.f;
+    constexpr int WL = DIMS == 3 ? 6 : 18;  // W values per thread: 16 x 81 or 64 x 72
+    float wv[WL];
+#pragma unroll
+    for (int k = 0; k < WL; ++k) {
+        const int i = (int)threadIdx.x + k * kMfmaBlock;
+        wv[k] = i < wcount ? w[i] : 0.f;
+    }
+    const float bv = (int)threadIdx.x < (int)g.Cout && b ? b[threadIdx.x] : 0.f;
+    if (begin < end) {
+        const int64_t sl = begin / rg.T, n = sl / rg.OO;
+        const int o = (int)(sl - n * rg.OO);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) fetch(rw[j], n, o + j);
+    }
+#pragma unroll
+    for (int k = 0; k < WL; ++k) {
+        const int i = (int)threadIdx.x + k * kMfmaBlock;
+        if (i < wcount) ring[i] = wv[k];
+    }
+    for (int i = (int)threadIdx.x + WL * kMfmaBlock; i < wcount; i += kMfmaBlock) ring[i] = w[i];
+    if ((int)threadIdx.x < (int)g.Cout) ring[wcount + threadIdx.x] = bv;
+    for (int i = (int)threadIdx.x + kMfmaBlock; i < (int)g.Cout; i += kMfmaBlock) ring[wcount + i] = b ? b[i] : 0.f;
     __syncthreads();
     // The packed taps depend on q alone: a table [4][KS] in LDS after the ring (and the
     // statistics area), read once per slice, keeps them out of the step loop's registers.
@@ -464,9 +492,13 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         sh[r] = 0.f;
     }
 
-    const int64_t total = (int64_t)g.N * rg.OO * rg.T;
-    const int64_t begin = total * blockIdx.x / gridDim.x;
-    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    if (begin < end) {  // the first run's window, loaded with W
+        const int64_t sl = begin / rg.T, n = sl / rg.OO;
+        const int o = (int)(sl - n * rg.OO);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) drop(rw[j], o + j);
+        __syncthreads();
+    }
     int64_t cur = -1;  // global slice (n * OO + o) whose window is in the ring
     for (int64_t t = begin; t < end;) {
         const int64_t sl = t / rg.T;
@@ -474,16 +506,17 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         const int o = (int)(sl - n * rg.OO);
         const int tlo = (int)(t - sl * rg.T);
         const int thi = (int)min((int64_t)rg.T, end - sl * rg.T);
-        if (sl != cur + 1 || o == 0) {  // new run: stage the whole window (synchronously)
+        if (cur >= 0 && (sl != cur + 1 || o == 0)) {  // a later run: stage its window slice by
+            // slice (the registers of three slices would stay reserved in the loop)
 #pragma unroll 1
             for (int j = o; j < o + 3; ++j) {
-                fetch(n, j);
-                drop(j);
+                fetch(pf, n, j);
+                drop(pf, j);
             }
             __syncthreads();
         }
         const bool ahead = (sl + 1) * rg.T < end && o + 1 < rg.OO;  // next step continues this run
-        if (ahead) fetch(n, o + 3);
+        if (ahead) fetch(pf, n, o + 3);
 
         // slot offsets of this step's taps
         int koff[KS];
@@ -579,7 +612,7 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         }
         if (STATS && pt0 >= 0)  // the slice's last step
             ring_tile_stats<MT, CL>(pacc, pt0, thi, shift, rg.inner_out, q, r16, run, sh);
-        if (ahead) drop(o + 3);
+        if (ahead) drop(pf, o + 3);
         __syncthreads();
         cur = sl;
         t = (sl + 1) * rg.T;
