@@ -1018,13 +1018,12 @@ def test_conv2d_bn_recompute_edges(dev, nra, orc, shape, misalign):
 
 
 def test_conv2d_bn_recompute_statistics_accuracy(dev, nra, orc):
-    # The recomputing batch-norm chain takes the statistics of channels with >= 16384 values
-    # from a conv with four bf16 partial products (x in two parts, W in three): each value is
-    # up to ~3e-5 of its scale off, from the rounding of x, which averages out. With momentum 1
-    # the running buffers receive the batch mean and unbiased variance themselves; they must
-    # match the fp64 oracle to 1e-6 (of the channel's std for the mean, relative for the
-    # variance). W in two parts biases the variance by ~1.9e-6 (measured), a one-product conv
-    # by ~4e-6.
+    # The recomputing batch-norm chain's statistics pass forms the apply pass's six bf16
+    # products and sums each lane's values shifted by its first one. With momentum 1 the
+    # running buffers receive the batch mean and unbiased variance themselves; they must match
+    # the fp64 oracle to 1e-6 (of the channel's std for the mean, relative for the variance).
+    # A conv from fewer products misses this: W in two parts biases the variance by ~1.9e-6
+    # (measured), a one-product conv by ~4e-6.
     g = np.random.Generator(np.random.PCG64(8080))
     x = g.standard_normal((16, 8, 64, 64)).astype(np.float32)
     bound = 1 / np.sqrt(72)
@@ -1043,6 +1042,49 @@ def test_conv2d_bn_recompute_statistics_accuracy(dev, nra, orc):
     _log("recompute statistics: mean err / std %.3e, var rel err %.3e" % (em, ev))
     assert em <= 1e-6
     assert ev <= 1e-6
+
+
+def test_conv2d_bn_recompute_offset_inputs(dev, nra, orc):
+    # x = 1 + 0.1 N(0,1) puts each channel's conv output up to 25 (median 6) standard
+    # deviations from zero (mean sum(w) + b, std 0.1 |w| ~ 0.06). The statistics pass sums each
+    # lane's values shifted by its first one, so the sums stay at the spread's scale; unshifted
+    # fp32 sums of squares over a lane's ~128 values would put the variance ~128 x 6e-8 x 25^2
+    # ~ 5e-3 off, and the outputs ~1e-3. The outputs must meet the 1e-4 gate (at larger offsets
+    # the conv's own fp32 accumulation, ~6e-8 of |y| per rounding, reaches the gate after the
+    # division by the std, whatever the statistics). With momentum 1 the running buffers receive
+    # the batch mean and unbiased variance: the mean must lie within the conv's error bound of
+    # the fp64 oracle's (2^-20 (sum |x||w| + |b|) per value, tested for the producer alone), the
+    # variance within 1e-5 relative.
+    g = np.random.Generator(np.random.PCG64(8181))
+    x = (1.0 + 0.1 * g.standard_normal((16, 8, 64, 64))).astype(np.float32)
+    bound = 1 / np.sqrt(72)
+    w = g.uniform(-bound, bound, (64, 8, 3, 3)).astype(np.float32)
+    b = g.uniform(-bound, bound, 64).astype(np.float32)
+    gm = g.uniform(0.5, 1.0, 64).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, 64).astype(np.float32)
+    rm = T(np.zeros(64, np.float32), dev)
+    rv = T(np.ones(64, np.float32), dev)
+    out = nra.conv_norm_epilogue_forward(T(x, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN,
+                                         gamma=T(gm, dev), beta=T(bt, dev),
+                                         running_mean=rm, running_var=rv, momentum=1.0)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=True, gamma=gm, beta=bt)
+    err = maxerr(H(out), ref)
+    c = orc.conv_k3(x, w, b)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    std = np.sqrt(var)
+    ratio = float(np.max(np.abs(mean) / std))
+    conv_bound = 2.0 ** -20 * (np.abs(w).reshape(64, -1).sum(1) * float(np.abs(x).max()) + np.abs(b))
+    count = c.size // 64
+    var_u = var * count / (count - 1)
+    em = np.abs(H(rm) - mean)
+    ev = float(np.max(np.abs(H(rv) - var_u) / var_u))
+    _log("recompute, offset inputs (|mean|/std up to %.1f): max_abs_err %.3e, mean err / std %.3e "
+         "(bound %.3e), var rel err %.3e" % (ratio, err, float(np.max(em / std)),
+                                             float(np.min(conv_bound / std)), ev))
+    assert ratio > 20
+    assert err <= TOL
+    assert np.all(em <= conv_bound + 1e-6 * std)
+    assert ev <= 1e-5
 
 
 def test_conv_chain_max_c_misaligned_out(dev, nra, orc):
