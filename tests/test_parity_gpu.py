@@ -1108,10 +1108,12 @@ def test_conv_chain_max_c_misaligned_out(dev, nra, orc):
 def test_graph_capture_and_replay(dev, nra, orc):
     # every launch of these entry points can be captured: no hipMemsetAsync (fill kernels
     # instead), no synchronization, regular launches. Capture instance norm (read-once
-    # pipelined), batch norm and the IN3d conv chain once (4 items: statistics from a pass over
-    # the conv output; 32 items, planar and channels last: statistics taken by the producer),
-    # then replay three times with eager changes of the inputs in between, checking every
-    # replay against the oracle.
+    # pipelined), batch norm, the IN3d conv chain (4 items: statistics from a pass over the
+    # conv output; 32 items, planar and channels last: statistics taken by the producer) and
+    # the 2-D 64-wide producer's two chains (batch norm by recomputation, whose statistics pass
+    # clears the tagged words the apply pass publishes; eval mode folded into W) once, then
+    # replay three times with eager changes of the inputs in between, checking every replay
+    # against the oracle.
     import torch
 
     g = np.random.Generator(np.random.PCG64(5150))
@@ -1125,8 +1127,14 @@ def test_graph_capture_and_replay(dev, nra, orc):
     xd = T(np.ascontiguousarray(i5["x"][:32]), dev)
     xdl = torch.empty((32, 16, 32, 32, 3), device=dev)
     yd, ydl = torch.empty((32, 14, 30, 30), device=dev), torch.empty((32, 14, 30, 30), device=dev)
+    i4 = synth.host_inputs(4)
+    xe = T(np.ascontiguousarray(i4["x"][:12]), dev)
+    we, be, ge, bte = T(i4["w"], dev), T(i4["b"], dev), T(i4["gamma"], dev), T(i4["beta"], dev)
+    rme = T(g.uniform(-0.5, 0.5, 64).astype(np.float32), dev)
+    rve = T(g.uniform(0.5, 2.0, 64).astype(np.float32), dev)
+    ye, yev = torch.empty((12, 64, 62, 62), device=dev), torch.empty((12, 64, 62, 62), device=dev)
     s = torch.cuda.Stream(device=dev)
-    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(5)]
+    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(7)]
     chain = dict(norm=nra.NR_NORM_INSTANCE, pre_mul=mc, clamp=(-1.0, 1.0), post_mul=mc,
                  reduce_max_c=True)
 
@@ -1137,6 +1145,10 @@ def test_graph_capture_and_replay(dev, nra, orc):
         nra.conv_norm_epilogue_forward(xd, wc, bc, yd, workspace=ws[3], stream=s, **chain)
         nra.conv_norm_epilogue_forward(xdl, wc, bc, ydl, workspace=ws[4], stream=s,
                                        channels_last=True, **chain)
+        nra.conv_norm_epilogue_forward(xe, we, be, ye, norm=nra.NR_NORM_BATCH_TRAIN, gamma=ge,
+                                       beta=bte, out_scale=2.0, workspace=ws[5], stream=s)
+        nra.conv_bn_eval_forward(xe, we, be, rme, rve, yev, gamma=ge, beta=bte, out_scale=2.0,
+                                 workspace=ws[6], stream=s)
 
     s.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(s):
@@ -1153,6 +1165,7 @@ def test_graph_capture_and_replay(dev, nra, orc):
             xc.mul_(-1.0)
             xd.mul_(-0.5).add_(0.125)
             xdl.copy_(xd.permute(0, 2, 3, 4, 1))
+            xe.mul_(0.75).add_(0.5)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -1166,8 +1179,13 @@ def test_graph_capture_and_replay(dev, nra, orc):
         rd = orc.conv_norm_epilogue(H(xd), i5["w"], i5["b"], batch=False, pre_mul=i5["mult"],
                                     clamp=(-1.0, 1.0), post_mul=i5["mult"], reduce_max_c=True)
         e4, e5 = maxerr(H(yd), rd), maxerr(H(ydl), rd)
-        _log("graph replay %d: max_abs_err %.3e %.3e %.3e %.3e %.3e" % (rep, e1, e2, e3, e4, e5))
-        assert max(e1, e2, e3, e4, e5) <= TOL
+        e6 = maxerr(H(ye), orc.conv_norm_epilogue(H(xe), i4["w"], i4["b"], batch=True,
+                                                  gamma=i4["gamma"], beta=i4["beta"], out_scale=2.0))
+        e7 = maxerr(H(yev), orc.conv_bn_eval(H(xe), i4["w"], i4["b"], H(rme), H(rve),
+                                             gamma=i4["gamma"], beta=i4["beta"], scale=2.0))
+        _log("graph replay %d: max_abs_err %.3e %.3e %.3e %.3e %.3e %.3e %.3e"
+             % (rep, e1, e2, e3, e4, e5, e6, e7))
+        assert max(e1, e2, e3, e4, e5, e6, e7) <= TOL
 
 
 def test_native_c_abi_roundtrip(dev, orc, tmp_path):
