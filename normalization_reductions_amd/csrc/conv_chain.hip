@@ -5,9 +5,15 @@
 // ow+kw] (cross-correlation, valid, stride 1). IN3d page (task l2_p79): the 3-D form adds a
 // depth tap; extents shrink by 2 along each axis.
 //
-// Three producers, picked per shape by launch_conv_k3:
-//   * conv2d_c8_mfma32_kernel: 2-D, C_in 8 -> C_out 64, W 64 (the batch-norm model's shape) on
-//     32x32x2 fp32 matrix instructions, persistent workgroups over LDS-staged boxes of rows;
+// Four producers, picked per shape by launch_conv_k3:
+//   * conv2d_c8_bf16x6_kernel: 2-D, C_in 8 -> C_out 64, W 64 (the batch-norm model's shape) on
+//     32x32x16 bf16 matrix instructions, each fp32 operand split exactly into three bf16 parts
+//     and six of their products summed in fp32; workgroups own equal ranges of boxes of 4
+//     output rows, staged in LDS, and store their tiles through a per-wave LDS transpose. Its
+//     modes run the batch-norm chain by recomputation (a statistics pass storing nothing, then
+//     the conv again with the normalize epilogue) and the eval chain (BN folded into W);
+//   * conv2d_c8_mfma32_kernel: the same shape on 32x32x2 fp32 matrix instructions
+//     (NORMRED_CONV=fp32);
 //   * conv_k3_ring_kernel: 2-D C_in 8 -> 64 of other widths and 3-D C_in 3 -> 16 (the IN3d
 //     model's shape) on 16x16x4 fp32 matrix instructions, persistent workgroups rolling a
 //     4-slice LDS ring over rows or depth planes;
