@@ -1017,6 +1017,39 @@ def test_conv2d_bn_recompute_edges(dev, nra, orc, shape, misalign):
     _check_running(rm, rv, rm_ref, rv_ref, "conv2d bn %s" % (shape,))
 
 
+@pytest.mark.parametrize("n,h", [(1, 6), (1, 66), (3, 10), (7, 34), (2, 36), (5, 20)])
+def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
+    # the 2-D 64-wide producer over boxes of 4 output rows: output heights 4, 64, 8, 32 fill
+    # every box, 34 and 18 end each batch item on a box of 2 rows (4 tiles for 8 tile slots:
+    # overlapping and repeated tiles, whose positions the statistics must count once); 1-7
+    # items put from one to a few boxes in each workgroup. Batch norm by recomputation (with
+    # running statistics) and the eval chain, both against the oracle.
+    g = np.random.Generator(np.random.PCG64(6000 + 97 * n + h))
+    x = (g.standard_normal((n, 8, h, 64)) * 1.5 - 0.25).astype(np.float32)
+    bound = 1 / np.sqrt(72)
+    w = g.uniform(-bound, bound, (64, 8, 3, 3)).astype(np.float32)
+    b = g.uniform(-bound, bound, 64).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, 64).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, 64).astype(np.float32)
+    rm0 = g.uniform(-0.2, 0.2, 64).astype(np.float32)
+    rv0 = g.uniform(0.5, 1.5, 64).astype(np.float32)
+    rm, rv = T(rm0, dev), T(rv0, dev)
+    out = nra.conv_norm_epilogue_forward(T(x, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN,
+                                         gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0,
+                                         running_mean=rm, running_var=rv, momentum=0.3)
+    err = maxerr(H(out), orc.conv_norm_epilogue(x, w, b, batch=True, gamma=gm, beta=bt, out_scale=2.0))
+    c = orc.conv_k3(x, w, b)
+    _, mean, var = orc.batch_norm_train(c, with_stats=True)
+    rm_ref, rv_ref = orc.bn_running_update(mean, var, c.size // 64, rm0, rv0, momentum=0.3)
+    _check_running(rm, rv, rm_ref, rv_ref, "conv2d 64-wide n %d h %d" % (n, h))
+    ev = nra.conv_bn_eval_forward(T(x, dev), T(w, dev), T(b, dev), T(rm0, dev), T(rv0, dev),
+                                  gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0)
+    err_ev = maxerr(H(ev), orc.conv_bn_eval(x, w, b, rm0, rv0, gamma=gm, beta=bt, scale=2.0))
+    _log("conv2d 64-wide n %d h %d: bn max_abs_err %.3e, eval %.3e" % (n, h, err, err_ev))
+    assert err <= TOL
+    assert err_ev <= TOL
+
+
 def test_conv2d_bn_recompute_statistics_accuracy(dev, nra, orc):
     # The recomputing batch-norm chain's statistics pass forms the apply pass's six bf16
     # products and sums each lane's values shifted by its first one. With momentum 1 the
