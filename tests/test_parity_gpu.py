@@ -1221,6 +1221,50 @@ def test_graph_capture_and_replay(dev, nra, orc):
         assert max(e1, e2, e3, e4, e5, e6, e7) <= TOL
 
 
+def test_concurrent_streams(dev, nra, orc):
+    # The persistent kernels wait only on workgroups that have started (units handed out in
+    # order; the Conv2d->BN apply pass waits on its lowest-numbered workgroups), so they need no
+    # co-residency of their whole grid. Two streams run them at once, three rounds with no
+    # synchronization between the launches: pipelined instance norm (4 parts per slice), batch
+    # norm on channels of 16 parts, and the Conv2d->BN chain, each with its own workspace.
+    # Every result must match the oracle and no exchange wait may have given up.
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(7070))
+    xi = T(g.standard_normal((8, 64, 256, 256)).astype(np.float32), dev)
+    xb = T((g.standard_normal((64, 64, 62, 62)) * 2 + 1).astype(np.float32), dev)
+    i4 = synth.host_inputs(4)
+    xc = T(np.ascontiguousarray(i4["x"][:32]), dev)
+    wc, bc, gc, btc = (T(i4[k], dev) for k in ("w", "b", "gamma", "beta"))
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    rounds = 3
+    outs = []
+    ws = []
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        yi, yb = torch.empty_like(xi), torch.empty_like(xb)
+        yc = torch.empty((32, 64, 62, 62), device=dev)
+        w3 = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(3)]
+        torch.cuda.synchronize()
+        nra.inorm_forward(xi, yi, workspace=w3[0], stream=s1)
+        nra.bn_train_forward(xb, yb, workspace=w3[1], stream=s2)
+        nra.conv_norm_epilogue_forward(xc, wc, bc, yc, norm=nra.NR_NORM_BATCH_TRAIN, gamma=gc,
+                                       beta=btc, out_scale=2.0, workspace=w3[2], stream=s1 if r % 2 else s2)
+        outs.append((yi, yb, yc))
+        ws += w3
+    torch.cuda.synchronize()
+    for w in ws:
+        assert nra.workspace_check(w) == 0
+    ri = orc.instance_norm(H(xi))
+    rb = orc.batch_norm_train(H(xb))
+    rc = orc.conv_norm_epilogue(i4["x"][:32], i4["w"], i4["b"], batch=True, gamma=i4["gamma"],
+                                beta=i4["beta"], out_scale=2.0)
+    for r, (yi, yb, yc) in enumerate(outs):
+        e1, e2, e3 = maxerr(H(yi), ri), maxerr(H(yb), rb), maxerr(H(yc), rc)
+        _log("concurrent streams round %d: max_abs_err %.3e %.3e %.3e" % (r, e1, e2, e3))
+        assert max(e1, e2, e3) <= TOL
+
+
 def test_native_c_abi_roundtrip(dev, orc, tmp_path):
     # a plain C++ program (tests/native/abi_roundtrip.cpp, built by build()) drives the C ABI
     # with hipMalloc'd buffers and its own stream; its outputs must match the oracle
