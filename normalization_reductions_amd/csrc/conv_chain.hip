@@ -150,6 +150,14 @@ __host__ __device__ inline int64_t ring_wg_of(int64_t t, int64_t total, int64_t 
     return ((t + 1) * G - 1) / total;
 }
 
+// Range index of workgroup b. Consecutive workgroup ids go round-robin over the 8 XCDs; ranges
+// are given out so that each XCD's workgroups hold consecutive ranges (G a multiple of 8), so
+// the input planes that neighbouring ranges share are read through the same L2.
+__device__ __forceinline__ int64_t ring_range_of(int64_t b, int64_t G)
+{
+    return G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
 // Chan's merge of a step's statistics b (b.n > 0) into a lane's running statistics a, with the
 // hardware reciprocal (1 ulp) for the weight: it runs once per tile step, inside the matrix
 // loop. The exact merge (chan_merge) combines lanes, waves and workgroups. An empty a takes b
@@ -299,7 +307,7 @@ __device__ __forceinline__ Stat shfl_xor_stat(Stat s, int off)
 
 // End of this workgroup's part of batch item n: the lanes of a wave holding the same channel
 // merge by a butterfly (lower lanes first), the waves of a channel tile in order of wm through
-// LDS, and one thread per channel writes slot j = blockIdx.x - first_wg(n) of (n, k). Every
+// LDS, and one thread per channel writes slot j = range - first_wg(n) of (n, k). Every
 // thread of the workgroup calls it.
 template <int WAVES_M, bool CL>
 __device__ __forceinline__ void ring_stats_flush(const ConvGeom& g, const ConvRing& rg,
@@ -334,8 +342,9 @@ __device__ __forceinline__ void ring_stats_flush(const ConvGeom& g, const ConvRi
     const int64_t tpn = (int64_t)rg.OO * rg.T;  // tiles per batch item
     const int64_t total = g.N * tpn;
     const int64_t first = ring_wg_of(n * tpn, total, gridDim.x);
-    const int64_t j = blockIdx.x - first;
-    const bool last = ring_wg_of((n + 1) * tpn - 1, total, gridDim.x) == (int64_t)blockIdx.x;
+    const int64_t wr = ring_range_of(blockIdx.x, gridDim.x);
+    const int64_t j = wr - first;
+    const bool last = ring_wg_of((n + 1) * tpn - 1, total, gridDim.x) == wr;
     for (int k = threadIdx.x; k < (int)g.Cout; k += kMfmaBlock) {
         Stat st = red[k];
         for (int m = 1; m < WAVES_M; ++m) st = chan_merge(st, red[m * (int)g.Cout + k]);
@@ -420,8 +429,9 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         }
     };
     const int64_t total = (int64_t)g.N * rg.OO * rg.T;
-    const int64_t begin = total * blockIdx.x / gridDim.x;
-    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    const int64_t wr = ring_range_of(blockIdx.x, gridDim.x);
+    const int64_t begin = total * wr / gridDim.x;
+    const int64_t end = total * (wr + 1) / gridDim.x;
 
     // This lane's B fragment (channel ch, taps 4s + q): weight, outer tap a (kd in 3-D, kh in
     // 2-D) and the offset of the tap inside one slot, packed as (a << 24) | offset. W is read
@@ -902,8 +912,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     const int nbox = (OH + B - 1) / B;
 
     const int64_t total = g.N * (int64_t)nbox;
-    const int64_t begin = total * blockIdx.x / gridDim.x;
-    const int64_t end = total * (blockIdx.x + 1) / gridDim.x;
+    const int64_t wr = ring_range_of(blockIdx.x, gridDim.x);  // ranges by XCD (see there)
+    const int64_t begin = total * wr / gridDim.x;
+    const int64_t end = total * (wr + 1) / gridDim.x;
     // staging item of this thread: window row, 4 columns, 4 channels (consecutive threads take
     // consecutive columns, so each channel's loads are coalesced)
     const int it = threadIdx.x;
