@@ -790,6 +790,13 @@ __attribute__((visibility("default"))) nr_status conv_bn_eval_forward(
     size_t off_b;
     const size_t need = bn_eval_layout(g, &off_b);
     if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
+    // the 2-D 64-wide matrix producer folds the statistics into W and b as it stages them
+    if (conv2d_c8_eval_ok(g, x, out)) {
+        const hipError_t e = launch_conv2d_c8_eval(g, x, w, b, running_mean, running_var, d->gamma,
+                                                   d->beta, d->eps, d->out_scale, out, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return NR_OK;
+    }
     float* wf = ws_at<float>(workspace, kHeaderBytes);
     float* bf = ws_at<float>(workspace, off_b);
     hipError_t e = launch_fold_bn_eval(g, w, b, running_mean, running_var, d->gamma, d->beta,

@@ -959,6 +959,20 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int nt = i / 96, sp = (i / 32) % 3, lane = 32 + i % 32;
         *reinterpret_cast<mu4*>(win + (((nt * kBfChunks + kBfChunks - 1) * 3 + sp) * 64 + lane) * 8) = mu4{0, 0, 0, 0};
     }
+    if (MODE == kC8Conv && e.fold_rv) {
+        // eval mode folded in, with the fold kernel's arithmetic: each channel's factor once per
+        // workgroup, while the W loads are in flight
+        __shared__ float fold_a[kC8Cout];
+        if (threadIdx.x < kC8Cout) {
+            const int k = threadIdx.x;
+            const float inv = 1.0f / sqrtf(e.fold_rv[k] + e.eps);
+            const float gm = e.gamma ? e.gamma[k] : 1.f;
+            fold_a[k] = gm * inv * e.out_scale;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) wv[k] = wv[k] * fold_a[((int)threadIdx.x + 256 * k) / kC8K];
+    }
 #pragma unroll
     for (int k = 0; k < WPT; ++k) {
         const int i = (int)threadIdx.x + 256 * k;
@@ -980,7 +994,17 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             for (int sp = 0; sp < 3; ++sp)
                 wb[nt][q][sp] = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(win + (((nt * kBfChunks + q) * 3 + sp) * 64 + l) * 8));
     __syncthreads();
-    const float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
+    float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
+    if (MODE == kC8Conv && e.fold_rv) {
+        auto fold_b = [&](int k, float bb) {
+            const float inv = 1.0f / sqrtf(e.fold_rv[k] + e.eps);
+            const float gm = e.gamma ? e.gamma[k] : 1.f;
+            const float bt = e.beta ? e.beta[k] : 0.f;
+            return ((bb - e.fold_rm[k]) * gm * inv + bt) * e.out_scale;
+        };
+        bias0 = fold_b(m, bias0);
+        bias1 = fold_b(32 + m, bias1);
+    }
     // per-channel factors of this lane's two channels m and 32 + m
     float pm0 = 1.f, pm1 = 1.f, mu0 = 0.f, mu1 = 0.f, A0 = 1.f, A1 = 1.f, B0 = 0.f, B1 = 0.f, q0 = 1.f, q1 = 1.f;
     if (MODE != kC8Conv && e.pre_mul) {
@@ -1572,6 +1596,31 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    return hipGetLastError();
+}
+
+bool conv2d_c8_eval_ok(const ConvGeom& g, const void* x, const void* out)
+{
+    const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+    return small && conv2d_c8_shape(g) && !conv_valu_forced() && !conv_fp32_forced() &&
+           (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+}
+
+hipError_t launch_conv2d_c8_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
+                                 const float* rm, const float* rv, const float* gamma,
+                                 const float* beta, float eps, float out_scale, float* out,
+                                 hipStream_t stream)
+{
+    if (!conv2d_c8_eval_ok(g, x, out)) return hipErrorInvalidValue;
+    C8Chain e;
+    e.fold_rm = rm;
+    e.fold_rv = rv;
+    e.gamma = gamma;
+    e.beta = beta;
+    e.eps = eps;
+    e.out_scale = out_scale;
+    conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)c8_grid(g)), dim3(256), 0, stream>>>(
+        g, x, w, b, out, e);
     return hipGetLastError();
 }
 

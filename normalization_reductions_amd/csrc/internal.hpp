@@ -133,6 +133,10 @@ struct C8Chain {
     int clamp = 0;
     float lo = 0.f, hi = 0.f;
     const float* post_mul = nullptr;
+    // eval mode folded into the conv (kC8Conv): when fold_rv is set, W and b are scaled per output
+    // channel k by gamma[k] / sqrt(fold_rv[k] + eps) * out_scale, b shifted by fold_rm[k] and beta
+    const float* fold_rm = nullptr;
+    const float* fold_rv = nullptr;
 };
 
 // The 2-D C_in 8 -> C_out 64, W = 64 shapes of the matrix producer (pointer alignment aside):
@@ -150,6 +154,13 @@ bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out);
 // Batch-norm chain by recomputation: statistics pass into e.part, fixed-order merge into
 // stats (and the running statistics), then the conv again with the chain epilogue into out.
 // Needs conv2d_c8_shape(g) and 16-byte aligned x and out.
+// Eval-mode batch norm folded into the 2-D matrix producer (no fold launch); false where that
+// producer does not take the call (the caller then folds W and b and calls launch_conv_k3).
+bool conv2d_c8_eval_ok(const ConvGeom& g, const void* x, const void* out);
+hipError_t launch_conv2d_c8_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
+                                 const float* rm, const float* rv, const float* gamma,
+                                 const float* beta, float eps, float out_scale, float* out,
+                                 hipStream_t stream);
 hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
                                      const float* b, float* out, C8Chain e, hipStream_t stream);
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
