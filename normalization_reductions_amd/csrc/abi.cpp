@@ -790,10 +790,10 @@ __attribute__((visibility("default"))) nr_status conv_bn_eval_forward(
     size_t off_b;
     const size_t need = bn_eval_layout(g, &off_b);
     if ((s = check_workspace(workspace, workspace_bytes, need, fn)) != NR_OK) return s;
-    // the 2-D 64-wide matrix producer folds the statistics into W and b as it stages them
-    if (conv2d_c8_eval_ok(g, x, out)) {
-        const hipError_t e = launch_conv2d_c8_eval(g, x, w, b, running_mean, running_var, d->gamma,
-                                                   d->beta, d->eps, d->out_scale, out, stream);
+    // the matrix producers fold the statistics into W and b as they stage them
+    if (conv_k3_eval_direct_ok(g, x, out)) {
+        const ConvFold fold{running_mean, running_var, d->gamma, d->beta, d->eps, d->out_scale};
+        const hipError_t e = launch_conv_k3_eval(g, x, w, b, fold, out, stream);
         if (e != hipSuccess) return hip_fail(e, fn);
         return NR_OK;
     }

@@ -373,7 +373,7 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
                                                                    const float* __restrict__ w,
                                                                    const float* __restrict__ b,
                                                                    float* __restrict__ c,
-                                                                   RingStats rs)
+                                                                   RingStats rs, ConvFold fold)
 {
     extern __shared__ float ring[];  // [4][Cin][inner_in], channels last: [4][inner_in][Cin]
     constexpr int KD = DIMS == 3 ? 3 : 1;
@@ -453,7 +453,26 @@ void conv_k3_ring_kernel(ConvGeom g, ConvRing rg,
         const int i = (int)threadIdx.x + k * kMfmaBlock;
         wv[k] = i < wcount ? w[i] : 0.f;
     }
-    const float bv = (int)threadIdx.x < (int)g.Cout && b ? b[threadIdx.x] : 0.f;
+    float bv = (int)threadIdx.x < (int)g.Cout && b ? b[threadIdx.x] : 0.f;
+    if (fold.rv) {
+        // eval mode folded in, with the fold kernel's arithmetic: channel factors once per
+        // workgroup (C_out <= 64 for the ring's shapes), while the W loads are in flight
+        __shared__ float fold_a[64];
+        if ((int)threadIdx.x < (int)g.Cout) {
+            const int k = threadIdx.x;
+            const float inv = 1.0f / sqrtf(fold.rv[k] + fold.eps);
+            const float gm = fold.gamma ? fold.gamma[k] : 1.f;
+            fold_a[k] = gm * inv * fold.scale;
+            const float bt = fold.beta ? fold.beta[k] : 0.f;
+            bv = ((bv - fold.rm[k]) * gm * inv + bt) * fold.scale;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WL; ++k) {
+            const int i = (int)threadIdx.x + k * kMfmaBlock;
+            if (i < wcount) wv[k] = wv[k] * fold_a[i / K];
+        }
+    }
     if (begin < end) {
         const int64_t sl = begin / rg.T, n = sl / rg.OO;
         const int o = (int)(sl - n * rg.OO);
@@ -1482,7 +1501,7 @@ int ring_grid(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu)
 template <int DIMS, int KS, int WAVES_N, int MT, int PF>
 hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, const float* x,
                        const float* w, const float* b, float* c, const RingStats* rs,
-                       hipStream_t stream)
+                       hipStream_t stream, const ConvFold* fold = nullptr)
 {
     // the ring, which first holds W (C_out x K floats) and the bias while the lanes take theirs;
     // with statistics, one Stat per (wave row, channel) after it; then the tap table
@@ -1492,6 +1511,8 @@ hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, co
     const int grid = ring_grid(g, rg, wgs_per_cu);
     const dim3 gd(grid), bd(kMfmaBlock);
     const RingStats none{nullptr, nullptr, 0};
+    const ConvFold nofold{nullptr, nullptr, nullptr, nullptr, 0.f, 1.f};
+    const ConvFold fd = fold ? *fold : nofold;
     // 3-D input planes of 32 x 32 (the IN3d model's) take a copy with the plane extents as
     // constants: its per-tile position arithmetic is a multiply and shift (2-3 % faster)
     const bool p32 = DIMS == 3 && g.W == 32 && g.H == 32;
@@ -1499,10 +1520,10 @@ hipError_t launch_ring(const ConvGeom& g, const ConvRing& rg, int wgs_per_cu, co
     do {                                                                                         \
         if (p32 && VEC)                                                                          \
             conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, VEC, CL, ST, DIMS == 3><<<gd, bd, lds, stream>>>( \
-                g, rg, x, w, b, c, rs ? *rs : none);                                             \
+                g, rg, x, w, b, c, rs ? *rs : none, fd);                                         \
         else                                                                                     \
             conv_k3_ring_kernel<DIMS, KS, WAVES_N, MT, PF, VEC, CL, ST><<<gd, bd, lds, stream>>>( \
-                g, rg, x, w, b, c, rs ? *rs : none);                                             \
+                g, rg, x, w, b, c, rs ? *rs : none, fd);                                         \
     } while (0)
     if (rs) {
         if (g.cl && rg.vec_in)
@@ -1599,29 +1620,40 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
     return hipGetLastError();
 }
 
-bool conv2d_c8_eval_ok(const ConvGeom& g, const void* x, const void* out)
+bool conv_k3_eval_direct_ok(const ConvGeom& g, const void* x, const void* out)
 {
     const bool small = g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
-    return small && conv2d_c8_shape(g) && !conv_valu_forced() && !conv_fp32_forced() &&
-           (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+    if (!small || conv_valu_forced()) return false;
+    if (conv2d_c8_shape(g))
+        return !conv_fp32_forced() && (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+    ConvRing rg;
+    const RingShape shape = ring_shape(g);
+    return (shape == kRing2d && make_ring(g, (const float*)x, (const float*)out, 1, &rg)) ||
+           (shape == kRing3d && make_ring(g, (const float*)x, (const float*)out, 3, &rg));
 }
 
-hipError_t launch_conv2d_c8_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
-                                 const float* rm, const float* rv, const float* gamma,
-                                 const float* beta, float eps, float out_scale, float* out,
-                                 hipStream_t stream)
+hipError_t launch_conv_k3_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
+                               const ConvFold& fold, float* out, hipStream_t stream)
 {
-    if (!conv2d_c8_eval_ok(g, x, out)) return hipErrorInvalidValue;
-    C8Chain e;
-    e.fold_rm = rm;
-    e.fold_rv = rv;
-    e.gamma = gamma;
-    e.beta = beta;
-    e.eps = eps;
-    e.out_scale = out_scale;
-    conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)c8_grid(g)), dim3(256), 0, stream>>>(
-        g, x, w, b, out, e);
-    return hipGetLastError();
+    if (!conv_k3_eval_direct_ok(g, x, out)) return hipErrorInvalidValue;
+    if (conv2d_c8_shape(g)) {
+        C8Chain e;
+        e.fold_rm = fold.rm;
+        e.fold_rv = fold.rv;
+        e.gamma = fold.gamma;
+        e.beta = fold.beta;
+        e.eps = fold.eps;
+        e.out_scale = fold.scale;
+        conv2d_c8_bf16x6_kernel<kC8B, kC8Conv><<<dim3((unsigned)c8_grid(g)), dim3(256), 0, stream>>>(
+            g, x, w, b, out, e);
+        return hipGetLastError();
+    }
+    ConvRing rg;
+    if (ring_shape(g) == kRing2d && make_ring(g, x, out, 1, &rg))
+        return launch_ring<2, 18, 4, 4, 1>(g, rg, kRingWgs2d, x, w, b, out, nullptr, stream, &fold);
+    if (ring_shape(g) == kRing3d && make_ring(g, x, out, 3, &rg))
+        return launch_ring<3, 21, 1, 2, 3>(g, rg, kRingWgs3d, x, w, b, out, nullptr, stream, &fold);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,

@@ -104,6 +104,17 @@ struct ConvRing {
     int vec_out;    // 16-byte output stores (aligned groups of 4 positions)
 };
 
+// Eval-mode batch norm folded into a conv producer as it stages W: output channel k's weights
+// scaled by gamma[k] / sqrt(rv[k] + eps) * scale, its bias to ((b[k] - rm[k]) * that + beta[k])
+// * scale (rv NULL: no fold).
+struct ConvFold {
+    const float* rm;
+    const float* rv;
+    const float* gamma;  // or NULL
+    const float* beta;   // or NULL
+    float eps, scale;
+};
+
 // Instance-norm statistics the ring producer takes of its own output: per batch item n, J slots
 // of partials per channel, merged in slot order by the reader.
 struct RingStats {
@@ -154,13 +165,12 @@ bool conv2d_c8_recompute(const ConvGeom& g, const void* x, const void* out);
 // Batch-norm chain by recomputation: statistics pass into e.part, fixed-order merge into
 // stats (and the running statistics), then the conv again with the chain epilogue into out.
 // Needs conv2d_c8_shape(g) and 16-byte aligned x and out.
-// Eval-mode batch norm folded into the 2-D matrix producer (no fold launch); false where that
-// producer does not take the call (the caller then folds W and b and calls launch_conv_k3).
-bool conv2d_c8_eval_ok(const ConvGeom& g, const void* x, const void* out);
-hipError_t launch_conv2d_c8_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
-                                 const float* rm, const float* rv, const float* gamma,
-                                 const float* beta, float eps, float out_scale, float* out,
-                                 hipStream_t stream);
+// Eval-mode batch norm folded into the matrix producers (the 2-D 64-wide one and the ring) as
+// they stage W, with no fold launch; false where no matrix producer takes the call (the caller
+// then folds W and b and calls launch_conv_k3).
+bool conv_k3_eval_direct_ok(const ConvGeom& g, const void* x, const void* out);
+hipError_t launch_conv_k3_eval(const ConvGeom& g, const float* x, const float* w, const float* b,
+                               const ConvFold& fold, float* out, hipStream_t stream);
 hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const float* w,
                                      const float* b, float* out, C8Chain e, hipStream_t stream);
 hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, const float* b,
