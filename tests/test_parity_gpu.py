@@ -1050,6 +1050,57 @@ def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
     assert err_ev <= TOL
 
 
+def _random_chain_cases(count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        kind = i % 3
+        if kind == 0:    # 2-D C_in 8 -> 64: the 64-wide matrix producer or the ring (other widths)
+            shape, cout = (int(g.integers(1, 6)), 8, int(g.integers(3, 30)), int(g.choice([64, int(g.integers(3, 80))]))), 64
+        elif kind == 1:  # 3-D C_in 3 -> 16: the ring
+            shape, cout = (int(g.integers(1, 4)), 3, int(g.integers(3, 10)), int(g.integers(3, 30)), int(g.integers(3, 30))), 16
+        else:            # other channel counts: the vector-ALU producer
+            shape, cout = (int(g.integers(1, 4)), int(g.integers(1, 5)), int(g.integers(3, 20)), int(g.integers(3, 20))), int(g.choice([4, 8, 32]))
+        batch = bool(g.integers(0, 2))
+        cases.append((i, shape, cout, batch, bool(g.integers(0, 2)), (not batch) and bool(g.integers(0, 2)),
+                      (not batch) and bool(g.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,shape,cout,batch,cl,red,clamp", _random_chain_cases(24, 9090))
+def test_conv_chain_random_cases(dev, nra, orc, i, shape, cout, batch, cl, red, clamp):
+    # seeded random shapes and flags through the conv -> normalize -> epilogue chain and the
+    # eval fold, every producer, both layouts, against the oracle
+    g = np.random.Generator(np.random.PCG64(4000 + i))
+    x = (g.standard_normal(shape) * g.uniform(0.5, 2) + g.uniform(-1, 1)).astype(np.float32)
+    cin = shape[1]
+    k = (3,) * (len(shape) - 2)
+    w = (g.standard_normal((cout, cin) + k) / np.sqrt(cin * 3 ** len(k))).astype(np.float32)
+    b = (g.standard_normal(cout) * 0.3).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, cout).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, cout).astype(np.float32)
+    pm = None if batch else g.uniform(0.5, 1.5, cout).astype(np.float32)
+    cl_rng = (-1.0, 1.0) if clamp else None
+    xin = np.moveaxis(x, 1, -1) if cl else x
+    out = nra.conv_norm_epilogue_forward(
+        T(xin, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN if batch else nra.NR_NORM_INSTANCE,
+        pre_mul=None if pm is None else T(pm, dev), gamma=T(gm, dev), beta=T(bt, dev), out_scale=1.5,
+        clamp=cl_rng, post_mul=None if pm is None else T(pm, dev), reduce_max_c=red, channels_last=cl)
+    ref = orc.conv_norm_epilogue(x, w, b, batch=batch, pre_mul=pm, gamma=gm, beta=bt, out_scale=1.5,
+                                 clamp=cl_rng, post_mul=pm, reduce_max_c=red)
+    got = H(out) if (red or not cl) else np.moveaxis(H(out), -1, 1)
+    rm = g.uniform(-0.3, 0.3, cout).astype(np.float32)
+    rv = g.uniform(0.5, 2.0, cout).astype(np.float32)
+    ev = nra.conv_bn_eval_forward(T(xin, dev), T(w, dev), T(b, dev), T(rm, dev), T(rv, dev),
+                                  gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0, channels_last=cl)
+    gev = H(ev) if not cl else np.moveaxis(H(ev), -1, 1)
+    err, err_ev = maxerr(got, ref), maxerr(gev, orc.conv_bn_eval(x, w, b, rm, rv, gamma=gm, beta=bt, scale=2.0))
+    _log("random chain %d %s cout %d batch %d cl %d max_c %d clamp %d: %.3e, eval %.3e"
+         % (i, shape, cout, batch, cl, red, clamp, err, err_ev))
+    assert err <= TOL
+    assert err_ev <= TOL
+
+
 def test_conv2d_bn_recompute_statistics_accuracy(dev, nra, orc):
     # The recomputing batch-norm chain's statistics pass forms the apply pass's six bf16
     # products and sums each lane's values shifted by its first one. With momentum 1 the
