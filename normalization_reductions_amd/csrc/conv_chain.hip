@@ -5,7 +5,7 @@
 // ow+kw] (cross-correlation, valid, stride 1). IN3d page (task l2_p79): the 3-D form adds a
 // depth tap; extents shrink by 2 along each axis.
 //
-// Four producers, picked per shape by launch_conv_k3:
+// Five producers, picked per shape by launch_conv_k3:
 //   * conv2d_c8_bf16x6_kernel: 2-D, C_in 8 -> C_out 64, W 64 (the batch-norm model's shape) on
 //     32x32x16 bf16 matrix instructions, each fp32 operand split exactly into three bf16 parts
 //     and six of their products summed in fp32; workgroups own equal ranges of boxes of 4
@@ -14,9 +14,15 @@
 //     the conv again with the normalize epilogue) and the eval chain (BN folded into W);
 //   * conv2d_c8_mfma32_kernel: the same shape on 32x32x2 fp32 matrix instructions
 //     (NORMRED_CONV=fp32);
-//   * conv_k3_ring_kernel: 2-D C_in 8 -> 64 of other widths and 3-D C_in 3 -> 16 (the IN3d
-//     model's shape) on 16x16x4 fp32 matrix instructions, persistent workgroups rolling a
-//     4-slice LDS ring over rows or depth planes;
+//   * conv3d_c3_bf16x6_kernel: 3-D, C_in 3 -> C_out 16 over 32 x 32 input planes (the IN3d
+//     model's shape) on 32x32x16 bf16 matrix instructions with the same exact splits, weights
+//     as the A operand (16 channels x two weight parts), one output row per tile; persistent
+//     workgroups roll a 3-slice LDS ring of split records over depth planes, and one LDS read
+//     per tap row feeds its three kw taps through a wave-wide lane shift. It also takes the
+//     instance statistics of its output, or folds eval-mode batch norm into W;
+//   * conv_k3_ring_kernel: 2-D C_in 8 -> 64 of other widths and 3-D C_in 3 -> 16 of other
+//     plane sizes on 16x16x4 fp32 matrix instructions, persistent workgroups rolling a 4-slice
+//     LDS ring over rows or depth planes (NORMRED_CONV=fp32 takes it for 32 x 32 planes too);
 //   * conv_k3_kernel: any other shape on the vector ALU, one lane per output position and KB
 //     output channels per thread in registers; weights are read with wave-uniform addresses and
 //     each loaded input value feeds KB fused multiply-adds.
@@ -1259,6 +1265,375 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// 3-D producer for C_in = 3 -> C_out = 16 over 32 x 32 input planes (the IN3d model's shape),
+// its fp32 products formed on the bf16 matrix pipe from the exact three-part splits of the 2-D
+// producer above. The operand roles are swapped against that producer: A holds the weights and
+// B the input, so one v_mfma_f32_32x32x16_bf16 covers 32 output positions (its columns) x 32
+// rows, and the rows hold the 16 output channels twice, rows 0..15 with one weight part and
+// rows 16..31 with another. Per K chunk four instructions, smallest products first,
+//     [Wh; Wm] x Xl,  [Wh; Wm] x Xm,  [Wl; 0] x Xh,  [Wh; Wm] x Xh,
+// leave hl + hm + lh + hh in the upper rows and ml + mm + mh in the lower ones; their sum holds
+// the six products of the 2-D producer, plus ml (which only adds accuracy). With 16 output
+// channels the fp32 instruction (16x16x4) needs 21 steps of 32 cycles per 16 positions; this
+// needs 28 of 32 cycles per 32 positions, 1.5x fewer matrix cycles.
+//
+// K order: chunk s covers taps 4s .. 4s + 3 (tap = 9 kd + 3 kh + kw; 27 taps and one padding
+// tap of zero weight): lanes 0..31 supply taps 4s and 4s + 1, lanes 32..63 taps 4s + 2 and
+// 4s + 3, each as 4 channels (the three input channels and a zero), so a tap of one split is
+// one 8-byte LDS read of a channels-last record. A and B map (lane half, element) to (tap,
+// channel) alike. D: lane l receives position l % 32, rows 8j + 4(l / 32) + r in register
+// 4j + r, so after adding the row halves it holds output channels 4(l / 32) + r and
+// 8 + 4(l / 32) + r (r = 0..3) of one position.
+//
+// Persistent form as the fp32 ring producer: a tile is one output row (30 positions; lanes 30
+// and 31 repeat lane 29's reads and store nothing), each output depth slice holds 30 of them,
+// and the grid splits the N * OD * 30 tiles into equal contiguous ranges, given out by XCD.
+// Row tiles cost no more matrix rounds than tiles of 32 consecutive positions would (29 per
+// slice: 4 rounds of 8 either way), and their reads are free of LDS bank conflicts: 32
+// consecutive positions cross a row, and the two lanes past the row's end hit the banks of the
+// row's first two records. The window of output slice o -- input slices o, o+1, o+2 -- sits in
+// LDS as the three bf16 splits of channels-last records: a ring of three 24 KB slots, so two
+// workgroups share a CU. The next input slice is loaded into registers during a step and split
+// into slice o's slot once every wave is done with it.
+// ---------------------------------------------------------------------------------------------
+constexpr int k3Pos = 900, k3Tiles = 30;  // positions and row tiles per output depth slice
+// ushorts of one split of one staged input slice, padded by 16 bytes: splits 8208 bytes apart
+// are read with one instruction each, straight into the operand's registers (at 8192 the
+// compiler pairs two splits of a tap into one read and then shuffles registers); the padding
+// keeps the staging's 16-byte writes aligned
+constexpr int k3SplitU = 1024 * 4 + 8;
+constexpr int k3SlotU = 3 * k3SplitU;
+constexpr int k3Chunks = 7;
+constexpr int k3Wgs = 2;                   // workgroups per CU (the LDS holds two rings)
+
+// K order. A tap row is (kd, kh), R = 3 kd + kh, holding taps 3R + kw. Lane half 0 takes rows
+// 0..3 and half 1 rows 4..7, each as kw = 0, 1, 2, so the halves run the same kw sequence; row 8
+// comes last, kw 0, 1 in half 0 and kw 2 and the padding tap (27, zero weight) in half 1. Tap j
+// (0..13) of half kk:
+__device__ __forceinline__ int k3_tap(int kk, int j)
+{
+    if (j < 12) return 3 * (4 * kk + j / 3) + j % 3;
+    return j == 12 ? (kk ? 26 : 24) : (kk ? 27 : 25);
+}
+
+// Lane l takes lane l + 1's value (a wave-wide shift; the last lane gets 0): tap kw + 1 of
+// output column c is tap kw of column c + 1, so one LDS read per tap row feeds all three kw.
+__device__ __forceinline__ unsigned k3_next_lane(unsigned v)
+{
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x130 /* wave_shl:1 */, 0xF, 0xF, true);
+}
+
+template <bool CL, bool STATS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const float* __restrict__ w,
+                             const float* __restrict__ b, float* __restrict__ c, RingStats rs,
+                             ConvFold fold)
+{
+    __shared__ __attribute__((aligned(16))) unsigned short ring3[3 * k3SlotU];
+    __shared__ float bias3[16];
+    __shared__ Stat red3[4 * 16];
+    const int tid = threadIdx.x;
+    const int l = tid & 63, wave = tid >> 6;
+    const int m = l & 31, kk = l >> 5;
+    const int D = (int)g.D, OD = (int)g.OD;
+    const int64_t SP = g.SP;
+    const int64_t total = g.N * (int64_t)OD * k3Tiles;
+    const int64_t G = gridDim.x;
+    const int64_t wr = ring_range_of(blockIdx.x, G);
+    const int64_t begin = total * wr / G;
+    const int64_t end = total * (wr + 1) / G;
+
+    // staging: thread t moves positions 4t .. 4t + 3 of an input slice, its three channels
+    auto fetch = [&](mf4(&f)[3], int64_t n, int z) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            f[k] = CL ? *reinterpret_cast<const mf4*>(x + ((n * D + z) * 1024) * 3 + 12 * tid + 4 * k)
+                      : *reinterpret_cast<const mf4*>(x + ((n * 3 + k) * D + z) * 1024 + 4 * tid);
+    };
+    auto drop = [&](const mf4(&f)[3], int z) {
+        unsigned r[24];  // the records of the thread's 4 positions: split sp in r[8 sp .. 8 sp + 7]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // channel ci of position 4t + j: planar f[ci][j]; channels last flat element 3j + ci
+            const float v0 = CL ? f[(3 * j) >> 2][(3 * j) & 3] : f[0][j];
+            const float v1 = CL ? f[(3 * j + 1) >> 2][(3 * j + 1) & 3] : f[1][j];
+            const float v2 = CL ? f[(3 * j + 2) >> 2][(3 * j + 2) & 3] : f[2][j];
+            split3x2(v0, v1, r[2 * j], r[8 + 2 * j], r[16 + 2 * j]);
+            split3x2(v2, 0.f, r[2 * j + 1], r[8 + 2 * j + 1], r[16 + 2 * j + 1]);
+        }
+        unsigned short* d = ring3 + (z % 3) * k3SlotU + 16 * tid;
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+            *reinterpret_cast<mu4*>(d + sp * k3SplitU) = mu4{r[8 * sp], r[8 * sp + 1], r[8 * sp + 2], r[8 * sp + 3]};
+            *reinterpret_cast<mu4*>(d + sp * k3SplitU + 8) = mu4{r[8 * sp + 4], r[8 * sp + 5], r[8 * sp + 6], r[8 * sp + 7]};
+        }
+    };
+
+    // W (16 x 81) with coalesced loads, then the first run's window behind it (the loads complete
+    // in order, so the W staging waits for W alone); eval mode folded in per channel as the
+    // fold kernel computes it
+    constexpr int WN = 16 * 81, WL = (WN + 255) / 256;
+    float wv[WL];
+#pragma unroll
+    for (int k = 0; k < WL; ++k) {
+        const int i = tid + 256 * k;
+        wv[k] = i < WN ? w[i] : 0.f;
+    }
+    float bv = tid < 16 && b ? b[tid] : 0.f;
+    if (fold.rv) {
+        __shared__ float fold_a3[16];
+        if (tid < 16) {
+            const float inv = 1.0f / sqrtf(fold.rv[tid] + fold.eps);
+            const float gm = fold.gamma ? fold.gamma[tid] : 1.f;
+            fold_a3[tid] = gm * inv * fold.scale;
+            const float bt = fold.beta ? fold.beta[tid] : 0.f;
+            bv = ((bv - fold.rm[tid]) * gm * inv + bt) * fold.scale;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WL; ++k) {
+            const int i = tid + 256 * k;
+            if (i < WN) wv[k] = wv[k] * fold_a3[i / 81];
+        }
+    }
+    mf4 rw[3][3];
+    if (begin < end) {
+        const int64_t sl = begin / k3Tiles, n = sl / OD;
+        const int o = (int)(sl - n * OD);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) fetch(rw[j], n, o + j);
+    }
+    float* wl = reinterpret_cast<float*>(ring3);  // free until the first window is staged
+#pragma unroll
+    for (int k = 0; k < WL; ++k) {
+        const int i = tid + 256 * k;
+        if (i < WN) wl[i] = wv[k];
+    }
+    if (tid < 16) bias3[tid] = bv;
+    __syncthreads();
+    // A operands: lane (m, kk) holds row m -- output channel m % 16, weight part [h | m] for
+    // rows 0..15 | 16..31 in pa, [l | 0] in pb -- at tap k3_tap(kk, 2s + e / 4), channel e % 4
+    const int co = m & 15, part = m >> 4;
+    bf8 pa[k3Chunks], pb[k3Chunks];
+#pragma unroll
+    for (int s = 0; s < k3Chunks; ++s) {
+        unsigned ua[8], ub[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tap = k3_tap(kk, 2 * s + (e >> 2)), ch = e & 3;
+            const float v = (tap < 27 && ch < 3) ? wl[co * 81 + ch * 27 + tap] : 0.f;
+            unsigned h, mm, lo;
+            split3(v, h, mm, lo);
+            ua[e] = part ? mm : h;
+            ub[e] = part ? 0u : lo;
+        }
+        pa[s] = __builtin_bit_cast(bf8, mu4{ua[0] | (ua[1] << 16), ua[2] | (ua[3] << 16),
+                                            ua[4] | (ua[5] << 16), ua[6] | (ua[7] << 16)});
+        pb[s] = __builtin_bit_cast(bf8, mu4{ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16),
+                                            ub[4] | (ub[5] << 16), ub[6] | (ub[7] << 16)});
+    }
+    float bias8[8];  // this lane's channels' bias, added to the finished sums
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        bias8[r] = bias3[4 * kk + r];
+        bias8[4 + r] = bias3[8 + 4 * kk + r];
+    }
+    __syncthreads();  // the W area becomes the first window
+    if (begin < end) {
+        const int64_t sl = begin / k3Tiles, n = sl / OD;
+        const int o = (int)(sl - n * OD);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) drop(rw[j], o + j);
+        __syncthreads();
+    }
+
+    // statistics of this lane's 8 channels over the current batch item, one value per channel
+    // and tile, by Welford's update with one count for all 8 (they share the positions). The
+    // first value becomes the mean exactly (1/1 is exact) and a constant channel adds exact
+    // zeros, so it keeps its value as the mean and M2 = 0.
+    float mean8[8], m28[8], cnt = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean8[i] = m28[i] = 0.f;
+    auto flush = [&](int64_t n) {
+        Stat st[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] = cnt > 0.f ? Stat{cnt, mean8[i], m28[i]} : stat_empty();
+        // the 32 lanes of a half hold the same 8 channels: butterfly, lower lanes first
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const Stat o = shfl_xor_stat(st[i], off);
+                st[i] = (l & off) ? chan_merge(o, st[i]) : chan_merge(st[i], o);
+            }
+        if (m == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) red3[wave * 16 + (i < 4 ? 4 * kk + i : 4 + 4 * kk + i)] = st[i];
+        }
+        __syncthreads();
+        const int64_t tpn = (int64_t)OD * k3Tiles;
+        const int64_t j = wr - ring_wg_of(n * tpn, total, G);
+        const bool last = ring_wg_of((n + 1) * tpn - 1, total, G) == wr;
+        if (tid < 16) {
+            Stat t = red3[tid];
+#pragma unroll
+            for (int v = 1; v < 4; ++v) t = chan_merge(t, red3[v * 16 + tid]);
+            const float pm = rs.pre_mul ? rs.pre_mul[tid] : 1.f;
+            float4* slot = rs.part + (n * rs.J) * 16 + tid;
+            slot[j * 16] = make_float4(t.n, mul_rn(t.mean, pm), t.m2 * pm * pm, 0.f);
+            if (last)
+                for (int64_t jj = j + 1; jj < rs.J; ++jj) slot[jj * 16] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        __syncthreads();
+        cnt = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mean8[i] = m28[i] = 0.f;
+    };
+
+    mf4 pf[3];
+    int64_t cur = -1;  // global slice (n * OD + o) whose window is in the ring
+    for (int64_t t = begin; t < end;) {
+        const int64_t sl = t / k3Tiles;
+        const int64_t n = sl / OD;
+        const int o = (int)(sl - n * OD);
+        const int tlo = (int)(t - sl * k3Tiles);
+        const int thi = (int)min((int64_t)k3Tiles, end - sl * k3Tiles);
+        if (cur >= 0 && (sl != cur + 1 || o == 0)) {  // a later run: stage its window
+#pragma unroll 1
+            for (int j = o; j < o + 3; ++j) {
+                fetch(pf, n, j);
+                drop(pf, j);
+            }
+            __syncthreads();
+        }
+        const bool ahead = (sl + 1) * k3Tiles < end && o + 1 < OD;  // the next step continues
+        if (ahead) fetch(pf, n, o + 3);
+
+        // this lane's tap rows in this step's window (slot of kd, then kh rows down)
+        const int sb0 = (o % 3) * k3SlotU, sb1 = ((o + 1) % 3) * k3SlotU, sb2 = ((o + 2) % 3) * k3SlotU;
+        auto rowoff = [&](int R) { return (R < 3 ? sb0 : R < 6 ? sb1 : sb2) + (R % 3) * 32 * 4; };
+        int roff[5];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) roff[i] = kk ? rowoff(4 + i) : rowoff(i);
+        roff[4] = rowoff(8);
+        float* cs = CL ? c + (n * OD + o) * (int64_t)k3Pos * 16 : c + n * 16 * SP + (int64_t)o * k3Pos;
+
+        for (int t0 = tlo + 2 * wave; t0 < thi; t0 += 8) {
+            int bp[2], p[2];
+            bool own[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int ti = t0 + mt;  // output row; ti == thi only as a wave's second tile
+                own[mt] = ti < thi && m < 30;
+                p[mt] = ti * 30 + m;
+                // lanes 30, 31 read input columns 30, 31 (their kw 0), which columns 28, 29
+                // take as kw 1, 2 through the lane shift
+                bp[mt] = ((ti < 30 ? ti : 29) * 32 + m) * 4;
+            }
+            mf16 acc[2] = {};
+            // the three splits of a tap row at kw 0 (one LDS read each), and at kw + 1 by the
+            // lane shift
+            typedef mu2 Tap[3];
+            auto rd = [&](int mt, int i, Tap& k) {
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp)
+                    k[sp] = *reinterpret_cast<const mu2*>(ring3 + bp[mt] + roff[i] + sp * k3SplitU);
+            };
+            auto shift = [&](const Tap& a, Tap& b) {
+#pragma unroll
+                for (int sp = 0; sp < 3; ++sp) b[sp] = mu2{k3_next_lane(a[sp].x), k3_next_lane(a[sp].y)};
+            };
+            // chunk s from its two taps: the four products, smallest first
+            auto chunk = [&](int s, int mt, const Tap& ta, const Tap& tb) {
+                const bf8 bh = __builtin_bit_cast(bf8, mu4{ta[0].x, ta[0].y, tb[0].x, tb[0].y});
+                const bf8 bm = __builtin_bit_cast(bf8, mu4{ta[1].x, ta[1].y, tb[1].x, tb[1].y});
+                const bf8 bl = __builtin_bit_cast(bf8, mu4{ta[2].x, ta[2].y, tb[2].x, tb[2].y});
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bl, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bm, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s], bh, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bh, acc[mt], 0, 0, 0);
+            };
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {  // rows 2pr, 2pr + 1 of each half: chunks 3pr .. 3pr + 2
+                Tap a0[2], a1[2], a2[2], b0[2], b1[2], b2[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    rd(mt, 2 * pr, a0[mt]);
+                    rd(mt, 2 * pr + 1, b0[mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    shift(a0[mt], a1[mt]);
+                    shift(a1[mt], a2[mt]);
+                    shift(b0[mt], b1[mt]);
+                    shift(b1[mt], b2[mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) chunk(3 * pr, mt, a0[mt], a1[mt]);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) chunk(3 * pr + 1, mt, a2[mt], b0[mt]);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) chunk(3 * pr + 2, mt, b1[mt], b2[mt]);
+            }
+            {  // row 8: kw 0, 1 in half 0; kw 2 and the padding tap in half 1
+                Tap c0[2], c1[2], c2[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) rd(mt, 4, c0[mt]);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    shift(c0[mt], c1[mt]);
+                    shift(c1[mt], c2[mt]);
+#pragma unroll
+                    for (int sp = 0; sp < 3; ++sp) c0[mt][sp] = kk ? c2[mt][sp] : c0[mt][sp];
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) chunk(6, mt, c0[mt], c1[mt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                // channels 4kk + r (v[r]) and 8 + 4kk + r (v[4 + r]) at position p
+                float v[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = (acc[mt][r] + acc[mt][8 + r]) + bias8[r];
+                    v[4 + r] = (acc[mt][4 + r] + acc[mt][12 + r]) + bias8[4 + r];
+                }
+                if (!own[mt]) continue;
+                if (CL) {
+                    float* dst = cs + (int64_t)p[mt] * 16 + 4 * kk;
+                    *reinterpret_cast<mf4*>(dst) = mf4{v[0], v[1], v[2], v[3]};
+                    *reinterpret_cast<mf4*>(dst + 8) = mf4{v[4], v[5], v[6], v[7]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        cs[(4 * kk + r) * SP + p[mt]] = v[r];
+                        cs[(8 + 4 * kk + r) * SP + p[mt]] = v[4 + r];
+                    }
+                }
+                if (STATS) {
+                    cnt += 1.f;
+                    const float rn = __builtin_amdgcn_rcpf(cnt);  // 1 ulp; exact at cnt = 1
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float d = v[i] - mean8[i];
+                        mean8[i] = fmaf(d, rn, mean8[i]);
+                        m28[i] = fmaf(d, v[i] - mean8[i], m28[i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with slot o % 3
+        if (ahead) {
+            drop(pf, o + 3);
+            __syncthreads();
+        }
+        cur = sl;
+        t = (sl + 1) * k3Tiles;
+        if (STATS && (t >= end || o + 1 == OD)) flush(n);  // this workgroup's part of item n
+    }
+}
+
 // Eval-mode batch norm folded into the conv (BN page, its eval-mode discussion): per output
 // channel k, a = gamma * scale / sqrt(rv + eps); W'[k][.] = W[k][.] * a and
 // b' = ((b - rm) * gamma / sqrt(rv + eps) + beta) * scale. One workgroup per channel.
@@ -1574,6 +1949,53 @@ int64_t c8_grid(const ConvGeom& g)
     const int64_t nbox = (g.OH + kC8B - 1) / kC8B;
     return std::min<int64_t>(std::min<int64_t>(g.N * nbox, (int64_t)device_cus() * wgs), kC8MaxGrid);
 }
+
+// The 3-D bf16 producer's shape: C_in 3 -> C_out 16 over 32 x 32 input planes.
+bool conv3d_c3_shape(const ConvGeom& g)
+{
+    return g.dims == 3 && g.Cin == 3 && g.Cout == 16 && g.H == 32 && g.W == 32 && g.D >= 3;
+}
+
+// ... and a call it takes: x and the output 16-byte aligned (its staging loads and
+// channels-last stores are 16-byte vectors); NORMRED_CONV=fp32 or valu picks the others.
+bool conv3d_c3_ok(const ConvGeom& g, const void* x, const void* c)
+{
+    return conv3d_c3_shape(g) && !conv_valu_forced() && !conv_fp32_forced() &&
+           ((uintptr_t)x | (uintptr_t)c) % 16 == 0;
+}
+
+int64_t c3_grid(const ConvGeom& g)
+{
+    int wgs = k3Wgs;
+    if (const char* e = getenv("NORMRED_CONV_WGS_PER_CU")) wgs = std::min(8, std::max(1, atoi(e)));
+    return std::max<int64_t>(1, std::min<int64_t>(g.N * g.OD * k3Tiles, (int64_t)device_cus() * wgs));
+}
+
+// Statistics slots per batch item of the 3-D bf16 producer (the bound of ring_slots_for).
+int64_t c3_slots(const ConvGeom& g)
+{
+    const int64_t L = g.OD * k3Tiles, total = g.N * L, m = total / c3_grid(g);
+    return L < 2 ? 1 : (L - 2) / m + 2;
+}
+
+hipError_t launch_conv3d_c3(const ConvGeom& g, const float* x, const float* w, const float* b,
+                            float* c, const RingStats* rs, const ConvFold* fold, hipStream_t stream)
+{
+    const dim3 gd((unsigned)c3_grid(g)), bd(256);
+    const RingStats none{nullptr, nullptr, 0};
+    const ConvFold nofold{nullptr, nullptr, nullptr, nullptr, 0.f, 1.f};
+    const RingStats r = rs ? *rs : none;
+    const ConvFold fd = fold ? *fold : nofold;
+    if (rs && g.cl)
+        conv3d_c3_bf16x6_kernel<true, true><<<gd, bd, 0, stream>>>(g, x, w, b, c, r, fd);
+    else if (rs)
+        conv3d_c3_bf16x6_kernel<false, true><<<gd, bd, 0, stream>>>(g, x, w, b, c, r, fd);
+    else if (g.cl)
+        conv3d_c3_bf16x6_kernel<true, false><<<gd, bd, 0, stream>>>(g, x, w, b, c, r, fd);
+    else
+        conv3d_c3_bf16x6_kernel<false, false><<<gd, bd, 0, stream>>>(g, x, w, b, c, r, fd);
+    return hipGetLastError();
+}
 }  // namespace
 
 // 16-byte output stores need every box to start on a multiple of 4 positions: kC8B * 62 is,
@@ -1626,6 +2048,7 @@ bool conv_k3_eval_direct_ok(const ConvGeom& g, const void* x, const void* out)
     if (!small || conv_valu_forced()) return false;
     if (conv2d_c8_shape(g))
         return !conv_fp32_forced() && (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+    if (conv3d_c3_ok(g, x, out)) return true;
     ConvRing rg;
     const RingShape shape = ring_shape(g);
     return (shape == kRing2d && make_ring(g, (const float*)x, (const float*)out, 1, &rg)) ||
@@ -1648,6 +2071,7 @@ hipError_t launch_conv_k3_eval(const ConvGeom& g, const float* x, const float* w
             g, x, w, b, out, e);
         return hipGetLastError();
     }
+    if (conv3d_c3_ok(g, x, out)) return launch_conv3d_c3(g, x, w, b, out, nullptr, &fold, stream);
     ConvRing rg;
     if (ring_shape(g) == kRing2d && make_ring(g, x, out, 1, &rg))
         return launch_ring<2, 18, 4, 4, 1>(g, rg, kRingWgs2d, x, w, b, out, nullptr, stream, &fold);
@@ -1678,6 +2102,7 @@ hipError_t launch_conv_k3(const ConvGeom& g, const float* x, const float* w, con
         }
         if (ring_shape(g) == kRing2d && make_ring(g, x, c, 1, &rg))
             return launch_ring<2, 18, 4, 4, 1>(g, rg, kRingWgs2d, x, w, b, c, nullptr, stream);
+        if (conv3d_c3_ok(g, x, c)) return launch_conv3d_c3(g, x, w, b, c, nullptr, nullptr, stream);
         if (ring_shape(g) == kRing3d && make_ring(g, x, c, 3, &rg))
             return launch_ring<3, 21, 1, 2, 3>(g, rg, kRingWgs3d, x, w, b, c, nullptr, stream);
     }
@@ -1786,6 +2211,7 @@ int64_t ring_stats_slots(const ConvGeom& g)
         if (!make_ring(g, probe, probe + mis, PF, &rg)) return 0;
         J = std::max(J, ring_slots_for(g, rg, kRingWgsStats));
     }
+    if (conv3d_c3_shape(g)) J = std::max(J, c3_slots(g));  // the 3-D bf16 producer's slots
     // small batches spread an item over many workgroups: past kRingMaxSlots slots the epilogue
     // workgroups would spend longer merging them than a statistics pass over c takes
     return J <= kRingMaxSlots ? J : 0;
@@ -1794,6 +2220,8 @@ int64_t ring_stats_slots(const ConvGeom& g)
 hipError_t launch_conv_k3_stats(const ConvGeom& g, const float* x, const float* w, const float* b,
                                 float* c, RingStats rs, hipStream_t stream)
 {
+    if (conv3d_c3_ok(g, x, c) && c3_slots(g) <= rs.J)
+        return launch_conv3d_c3(g, x, w, b, c, &rs, nullptr, stream);
     const RingShape shape = ring_shape(g);
     ConvRing rg;
     if (shape == kRing2d && make_ring(g, x, c, 1, &rg) && ring_slots_for(g, rg, kRingWgsStats) <= rs.J)

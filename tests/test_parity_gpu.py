@@ -1050,6 +1050,67 @@ def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
     assert err_ev <= TOL
 
 
+# The 3-D bf16 producer's shape (C_in 3 -> C_out 16 over 32 x 32 input planes) at sizes that
+# give workgroups ranges of one tile (one output row) up to several output slices, ranges
+# crossing batch items, a single output slice (D = 3), and the many statistics slots of small
+# batches; every plan on top of it: instance norm with and without the channel max, batch
+# norm, and the eval fold
+C3_CASES = [(1, 3), (2, 5), (3, 4), (5, 7), (16, 4), (8, 16)]
+
+
+@pytest.mark.parametrize("cl", [False, True])
+@pytest.mark.parametrize("n,d", C3_CASES)
+def test_conv3d_32x32_planes(dev, nra, orc, n, d, cl):
+    g = np.random.Generator(np.random.PCG64(7000 + 31 * n + d))
+    x = (g.standard_normal((n, 3, d, 32, 32)) * 1.3 + 0.4).astype(np.float32)
+    w = (g.standard_normal((16, 3, 3, 3, 3)) / 9).astype(np.float32)
+    b = (g.standard_normal(16) * 0.3).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, 16).astype(np.float32)
+    bt = g.uniform(-0.5, 0.5, 16).astype(np.float32)
+    pm = g.uniform(0.5, 1.5, 16).astype(np.float32)
+    xin = np.moveaxis(x, 1, -1) if cl else x
+    for batch, red in ((False, True), (False, False), (True, False)):
+        out = nra.conv_norm_epilogue_forward(
+            T(xin, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN if batch else nra.NR_NORM_INSTANCE,
+            pre_mul=None if batch else T(pm, dev), gamma=T(gm, dev), beta=T(bt, dev), out_scale=1.5,
+            clamp=None if batch else (-1.0, 1.0), post_mul=None if batch else T(pm, dev),
+            reduce_max_c=red, channels_last=cl)
+        ref = orc.conv_norm_epilogue(x, w, b, batch=batch, pre_mul=None if batch else pm, gamma=gm,
+                                     beta=bt, out_scale=1.5, clamp=None if batch else (-1.0, 1.0),
+                                     post_mul=None if batch else pm, reduce_max_c=red)
+        got = H(out) if (red or not cl) else np.moveaxis(H(out), -1, 1)
+        err = maxerr(got, ref)
+        _log("conv3d 32x32 N %d D %d cl %d batch %d max_c %d: %.3e" % (n, d, cl, batch, red, err))
+        assert err <= TOL
+    rm = g.uniform(-0.3, 0.3, 16).astype(np.float32)
+    rv = g.uniform(0.5, 2.0, 16).astype(np.float32)
+    ev = nra.conv_bn_eval_forward(T(xin, dev), T(w, dev), T(b, dev), T(rm, dev), T(rv, dev),
+                                  gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0, channels_last=cl)
+    gev = H(ev) if not cl else np.moveaxis(H(ev), -1, 1)
+    err = maxerr(gev, orc.conv_bn_eval(x, w, b, rm, rv, gamma=gm, beta=bt, scale=2.0))
+    _log("conv3d 32x32 N %d D %d cl %d eval: %.3e" % (n, d, cl, err))
+    assert err <= TOL
+
+
+def test_conv3d_32x32_matches_fp32_ring(dev, nra, orc, monkeypatch):
+    # the bf16-split producer and the fp32 ring (NORMRED_CONV=fp32) on the IN3d model's shape:
+    # both within the tolerance of the oracle on sampled batch items, and of each other everywhere
+    import synth
+
+    i5 = synth.host_inputs(5)
+    x, w, b = T(i5["x"], dev), T(i5["w"], dev), T(i5["b"], dev)
+    rm = T(np.linspace(-0.2, 0.2, 16).astype(np.float32), dev)
+    rv = T(np.linspace(0.5, 1.5, 16).astype(np.float32), dev)
+    got = H(nra.conv_bn_eval_forward(x, w, b, rm, rv))
+    monkeypatch.setenv("NORMRED_CONV", "fp32")
+    ring = H(nra.conv_bn_eval_forward(x, w, b, rm, rv))
+    monkeypatch.delenv("NORMRED_CONV")
+    assert maxerr(got, ring) <= TOL
+    for n in (0, 77, 127):
+        ref = orc.conv_bn_eval(i5["x"][n:n + 1], i5["w"], i5["b"], H(rm), H(rv))
+        assert maxerr(got[n:n + 1], ref) <= TOL
+
+
 def _random_chain_cases(count, seed):
     g = np.random.Generator(np.random.PCG64(seed))
     cases = []
