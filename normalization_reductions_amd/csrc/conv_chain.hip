@@ -1352,7 +1352,9 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                       : *reinterpret_cast<const mf4*>(x + ((n * 3 + k) * D + z) * 1024 + 4 * tid);
     };
     auto drop = [&](const mf4(&f)[3], int z) {
-        unsigned r[24];  // the records of the thread's 4 positions: split sp in r[8 sp .. 8 sp + 7]
+        // the records of the thread's 4 positions: split sp in r[8 sp .. 8 sp + 7]; the fourth
+        // channel is 1 (its h part; 0 in m and l), which tap 0 weighs by the bias
+        unsigned r[24];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // channel ci of position 4t + j: planar f[ci][j]; channels last flat element 3j + ci
@@ -1360,7 +1362,7 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             const float v1 = CL ? f[(3 * j + 1) >> 2][(3 * j + 1) & 3] : f[1][j];
             const float v2 = CL ? f[(3 * j + 2) >> 2][(3 * j + 2) & 3] : f[2][j];
             split3x2(v0, v1, r[2 * j], r[8 + 2 * j], r[16 + 2 * j]);
-            split3x2(v2, 0.f, r[2 * j + 1], r[8 + 2 * j + 1], r[16 + 2 * j + 1]);
+            split3x2(v2, 1.f, r[2 * j + 1], r[8 + 2 * j + 1], r[16 + 2 * j + 1]);
         }
         unsigned short* d = ring3 + (z % 3) * k3SlotU + 16 * tid;
 #pragma unroll
@@ -1422,7 +1424,8 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int tap = k3_tap(kk, 2 * s + (e >> 2)), ch = e & 3;
-            const float v = (tap < 27 && ch < 3) ? wl[co * 81 + ch * 27 + tap] : 0.f;
+            // channel 3 of tap 0 carries the bias (every record's fourth channel is 1)
+            const float v = tap >= 27 ? 0.f : ch < 3 ? wl[co * 81 + ch * 27 + tap] : tap == 0 ? bias3[co] : 0.f;
             unsigned h, mm, lo;
             split3(v, h, mm, lo);
             ua[e] = part ? mm : h;
@@ -1432,12 +1435,6 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                                             ua[4] | (ua[5] << 16), ua[6] | (ua[7] << 16)});
         pb[s] = __builtin_bit_cast(bf8, mu4{ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16),
                                             ub[4] | (ub[5] << 16), ub[6] | (ub[7] << 16)});
-    }
-    float bias8[8];  // this lane's channels' bias, added to the finished sums
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        bias8[r] = bias3[4 * kk + r];
-        bias8[4 + r] = bias3[8 + 4 * kk + r];
     }
     __syncthreads();  // the W area becomes the first window
     if (begin < end) {
@@ -1456,17 +1453,35 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
     for (int i = 0; i < 8; ++i) mean8[i] = m28[i] = 0.f;
     auto flush = [&](int64_t n) {
+        // The 32 lanes of a half hold the same 8 channels, lanes 0..29 with the same count and
+        // lanes 30, 31 with none. Each lane's (count, mean, M2) becomes sums shifted by the
+        // mean P of the half's lane 0: S1 = c (mean - P), S2 = M2 + c (mean - P)^2; a butterfly
+        // adds them (no divisions), and lane 0 turns the totals back into (count, mean, M2). A
+        // constant channel has every mean equal to P, so its sums are exact zeros.
         Stat st[8];
+        float P[8], s1[8], s2[8], nt = cnt;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] = cnt > 0.f ? Stat{cnt, mean8[i], m28[i]} : stat_empty();
-        // the 32 lanes of a half hold the same 8 channels: butterfly, lower lanes first
+        for (int i = 0; i < 8; ++i) {
+            P[i] = __shfl(mean8[i], l & 32);
+            const float d = cnt > 0.f ? mean8[i] - P[i] : 0.f;
+            s1[i] = cnt * d;
+            s2[i] = fmaf(s1[i], d, m28[i]);
+        }
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1)
+        for (int off = 1; off < 32; off <<= 1) {
+            nt += __shfl_xor(nt, off);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const Stat o = shfl_xor_stat(st[i], off);
-                st[i] = (l & off) ? chan_merge(o, st[i]) : chan_merge(st[i], o);
+                s1[i] += __shfl_xor(s1[i], off);
+                s2[i] += __shfl_xor(s2[i], off);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float md = nt > 0.f ? s1[i] / nt : 0.f;
+            const float v = s2[i] - s1[i] * md;  // >= 0 but for rounding
+            st[i] = nt > 0.f ? Stat{nt, P[i] + md, v < 0.f ? 0.f : v} : stat_empty();
+        }
         if (m == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) red3[wave * 16 + (i < 4 ? 4 * kk + i : 4 + 4 * kk + i)] = st[i];
@@ -1516,8 +1531,17 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         int roff[5];
 #pragma unroll
         for (int i = 0; i < 4; ++i) roff[i] = kk ? rowoff(4 + i) : rowoff(i);
-        roff[4] = rowoff(8);
-        float* cs = CL ? c + (n * OD + o) * (int64_t)k3Pos * 16 : c + n * 16 * SP + (int64_t)o * k3Pos;
+        // row 8: half 1 reads it two columns right (its kw 2, then the padding tap as kw 3); the
+        // lanes past the row (30, 31) stay inside it at column 31
+        roff[4] = rowoff(8) + (kk ? (min(m + 2, 31) - m) * 4 : 0);
+        // stores through a buffer resource over batch item n's output (16 SP floats; the
+        // launcher keeps them below 2^31 bytes): the lane's byte offset in a register, the
+        // channel's in a scalar register, so no store needs its own address arithmetic.
+        // Planar: channel r (lane half 0) or 4 + r (half 1), then 8 + those, at o * 900 + p;
+        // channels last: position o * 900 + p's channels 4kk .. 4kk + 3 and 8 + those.
+        const __amdgpu_buffer_rsrc_t cres = __builtin_amdgcn_make_buffer_rsrc(
+            c + n * 16 * SP, 0, (int)(16 * SP * 4), 0x00020000 /* 32-bit data format */);
+        const uint32_t lane_base = CL ? (uint32_t)(o * k3Pos * 64 + 16 * kk) : (uint32_t)(o * k3Pos * 4) + (kk ? (uint32_t)(16 * SP) : 0u);
 
         for (int t0 = tlo + 2 * wave; t0 < thi; t0 += 8) {
             int bp[2], p[2];
@@ -1576,17 +1600,12 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) chunk(3 * pr + 2, mt, b1[mt], b2[mt]);
             }
-            {  // row 8: kw 0, 1 in half 0; kw 2 and the padding tap in half 1
-                Tap c0[2], c1[2], c2[2];
+            {  // row 8: kw 0, 1 in half 0; kw 2 and the padding tap in half 1 (read 2 columns right)
+                Tap c0[2], c1[2];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) rd(mt, 4, c0[mt]);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    shift(c0[mt], c1[mt]);
-                    shift(c1[mt], c2[mt]);
-#pragma unroll
-                    for (int sp = 0; sp < 3; ++sp) c0[mt][sp] = kk ? c2[mt][sp] : c0[mt][sp];
-                }
+                for (int mt = 0; mt < 2; ++mt) shift(c0[mt], c1[mt]);
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) chunk(6, mt, c0[mt], c1[mt]);
             }
@@ -1596,19 +1615,20 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 float v[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v[r] = (acc[mt][r] + acc[mt][8 + r]) + bias8[r];
-                    v[4 + r] = (acc[mt][4 + r] + acc[mt][12 + r]) + bias8[4 + r];
+                    v[r] = acc[mt][r] + acc[mt][8 + r];
+                    v[4 + r] = acc[mt][4 + r] + acc[mt][12 + r];
                 }
                 if (!own[mt]) continue;
                 if (CL) {
-                    float* dst = cs + (int64_t)p[mt] * 16 + 4 * kk;
-                    *reinterpret_cast<mf4*>(dst) = mf4{v[0], v[1], v[2], v[3]};
-                    *reinterpret_cast<mf4*>(dst + 8) = mf4{v[4], v[5], v[6], v[7]};
+                    const int off = (int)(lane_base + 64u * (uint32_t)p[mt]);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(mu4, mf4{v[0], v[1], v[2], v[3]}), cres, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(mu4, mf4{v[4], v[5], v[6], v[7]}), cres, off, 32, 0);
                 } else {
+                    const int off = (int)(lane_base + 4u * (uint32_t)p[mt]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        cs[(4 * kk + r) * SP + p[mt]] = v[r];
-                        cs[(8 + 4 * kk + r) * SP + p[mt]] = v[4 + r];
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), cres, off, (int)(r * SP * 4), 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[4 + r]), cres, off, (int)((8 + r) * SP * 4), 0);
                     }
                 }
                 if (STATS) {
@@ -1953,7 +1973,8 @@ int64_t c8_grid(const ConvGeom& g)
 // The 3-D bf16 producer's shape: C_in 3 -> C_out 16 over 32 x 32 input planes.
 bool conv3d_c3_shape(const ConvGeom& g)
 {
-    return g.dims == 3 && g.Cin == 3 && g.Cout == 16 && g.H == 32 && g.W == 32 && g.D >= 3;
+    return g.dims == 3 && g.Cin == 3 && g.Cout == 16 && g.H == 32 && g.W == 32 && g.D >= 3 &&
+           g.SP * 16 * 4 < (1LL << 31);
 }
 
 // ... and a call it takes: x and the output 16-byte aligned (its staging loads and
