@@ -1271,20 +1271,20 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 // producer above. The operand roles are swapped against that producer: A holds the weights and
 // B the input, so one v_mfma_f32_32x32x16_bf16 covers 32 output positions (its columns) x 32
 // rows, and the rows hold the 16 output channels twice, rows 0..15 with one weight part and
-// rows 16..31 with another. Per K chunk four instructions, smallest products first,
-//     [Wh; Wm] x Xl,  [Wh; Wm] x Xm,  [Wl; 0] x Xh,  [Wh; Wm] x Xh,
-// leave hl + hm + lh + hh in the upper rows and ml + mm + mh in the lower ones; their sum holds
-// the six products of the 2-D producer, plus ml (which only adds accuracy). With 16 output
-// channels the fp32 instruction (16x16x4) needs 21 steps of 32 cycles per 16 positions; this
-// needs 28 of 32 cycles per 32 positions, 1.5x fewer matrix cycles.
+// rows 16..31 with another. A tap contributes 12 K elements, its three channels' splits
+// (xh, xm, xl, xh), weighted (Wh, Wh, Wh, Wl) in the upper rows and (Wm, Wm, Wm, 0) in the lower
+// ones: the upper rows sum hh + hm + hl + lh, the lower ones mh + mm + ml, and the two halves
+// added hold the six products of the 2-D producer plus ml (which only adds accuracy). With 16
+// output channels the fp32 instruction (16x16x4) needs 21 steps of 32 cycles per 16 positions;
+// this needs 21 of 32 cycles per 32 positions (28 taps x 12 / 16), 2x fewer matrix cycles.
 //
-// K order: chunk s covers taps 4s .. 4s + 3 (tap = 9 kd + 3 kh + kw; 27 taps and one padding
-// tap of zero weight): lanes 0..31 supply taps 4s and 4s + 1, lanes 32..63 taps 4s + 2 and
-// 4s + 3, each as 4 channels (the three input channels and a zero), so a tap of one split is
-// one 8-byte LDS read of a channels-last record. A and B map (lane half, element) to (tap,
-// channel) alike. D: lane l receives position l % 32, rows 8j + 4(l / 32) + r in register
-// 4j + r, so after adding the row halves it holds output channels 4(l / 32) + r and
-// 8 + 4(l / 32) + r (r = 0..3) of one position.
+// K order: each lane half walks its own sequence of 14 taps (below), 12 elements a tap, 8
+// elements an instruction, so two taps fill three instructions. A staged record -- one input
+// position, 24 bytes -- holds a tap's 12 elements as three 8-byte pieces in three areas of the
+// slot ([h0 h1 h2 m0], [m1 m2 l0 l1], [l2 h0 h1 h2]), each one LDS read. A and B map (lane
+// half, element) to (tap, channel, part) alike. D: lane l receives position l % 32, rows
+// 8j + 4(l / 32) + r in register 4j + r, so after adding the row halves it holds output
+// channels 4(l / 32) + r and 8 + 4(l / 32) + r (r = 0..3) of one position.
 //
 // Persistent form as the fp32 ring producer: a tile is one output row (30 positions; lanes 30
 // and 31 repeat lane 29's reads and store nothing), each output depth slice holds 30 of them,
@@ -1304,13 +1304,14 @@ constexpr int k3Pos = 900, k3Tiles = 30;  // positions and row tiles per output 
 // keeps the staging's 16-byte writes aligned
 constexpr int k3SplitU = 1024 * 4 + 8;
 constexpr int k3SlotU = 3 * k3SplitU;
-constexpr int k3Chunks = 7;
+constexpr int k3Chunks = 7;  // tap pairs per lane half
+constexpr int k3Ops = 21;    // matrix instructions per tile: 14 taps x 12 elements / 8
 constexpr int k3Wgs = 2;                   // workgroups per CU (the LDS holds two rings)
 
-// K order. A tap row is (kd, kh), R = 3 kd + kh, holding taps 3R + kw. Lane half 0 takes rows
-// 0..3 and half 1 rows 4..7, each as kw = 0, 1, 2, so the halves run the same kw sequence; row 8
-// comes last, kw 0, 1 in half 0 and kw 2 and the padding tap (27, zero weight) in half 1. Tap j
-// (0..13) of half kk:
+// Tap sequence of a lane half. A tap row is (kd, kh), R = 3 kd + kh, holding taps 3R + kw. Half
+// 0 takes rows 0..3 and half 1 rows 4..7, each as kw = 0, 1, 2, so the halves run the same kw
+// sequence; row 8 comes last, kw 0, 1 in half 0 and kw 2 and the padding tap (27, zero weight)
+// in half 1. Tap j (0..13) of half kk:
 __device__ __forceinline__ int k3_tap(int kk, int j)
 {
     if (j < 12) return 3 * (4 * kk + j / 3) + j % 3;
@@ -1352,17 +1353,25 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                       : *reinterpret_cast<const mf4*>(x + ((n * 3 + k) * D + z) * 1024 + 4 * tid);
     };
     auto drop = [&](const mf4(&f)[3], int z) {
-        // the records of the thread's 4 positions: split sp in r[8 sp .. 8 sp + 7]; the fourth
-        // channel is 1 (its h part; 0 in m and l), which tap 0 weighs by the bias
+        // the records of the thread's 4 positions: area a in r[8 a .. 8 a + 7], position j's
+        // 8 bytes at 2j, 2j + 1 (bf16 pairs, the first element in the low half)
         unsigned r[24];
+        auto pk = [](unsigned lo, unsigned hi) { return (lo & 0xFFFFu) | (hi << 16); };
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // channel ci of position 4t + j: planar f[ci][j]; channels last flat element 3j + ci
             const float v0 = CL ? f[(3 * j) >> 2][(3 * j) & 3] : f[0][j];
             const float v1 = CL ? f[(3 * j + 1) >> 2][(3 * j + 1) & 3] : f[1][j];
             const float v2 = CL ? f[(3 * j + 2) >> 2][(3 * j + 2) & 3] : f[2][j];
-            split3x2(v0, v1, r[2 * j], r[8 + 2 * j], r[16 + 2 * j]);
-            split3x2(v2, 1.f, r[2 * j + 1], r[8 + 2 * j + 1], r[16 + 2 * j + 1]);
+            unsigned h01, m01, l01, h2, m2, l2;  // channels 0, 1 packed; channel 2 in the low half
+            split3x2(v0, v1, h01, m01, l01);
+            split3x2(v2, 0.f, h2, m2, l2);
+            r[2 * j] = h01;                          // h0 h1
+            r[2 * j + 1] = pk(h2, m01);              // h2 m0
+            r[8 + 2 * j] = pk(m01 >> 16, m2);        // m1 m2
+            r[8 + 2 * j + 1] = l01;                  // l0 l1
+            r[16 + 2 * j] = pk(l2, h01);             // l2 h0
+            r[16 + 2 * j + 1] = pk(h01 >> 16, h2);   // h1 h2
         }
         unsigned short* d = ring3 + (z % 3) * k3SlotU + 16 * tid;
 #pragma unroll
@@ -1414,27 +1423,32 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     }
     if (tid < 16) bias3[tid] = bv;
     __syncthreads();
-    // A operands: lane (m, kk) holds row m -- output channel m % 16, weight part [h | m] for
-    // rows 0..15 | 16..31 in pa, [l | 0] in pb -- at tap k3_tap(kk, 2s + e / 4), channel e % 4
+    // A operands: lane (m, kk) holds row m -- output channel m % 16, part 0 (rows 0..15) or 1
+    // (rows 16..31) -- for K elements 8j .. 8j + 7 of its half: element q is element q % 12 of
+    // tap k3_tap(kk, q / 12), channel q % 3 of x part (q % 12) / 3 (h, m, l, h), weighted
+    // (Wh, Wh, Wh, Wl) in part 0 and (Wm, Wm, Wm, 0) in part 1
     const int co = m & 15, part = m >> 4;
-    bf8 pa[k3Chunks], pb[k3Chunks];
+    bf8 pa[k3Ops];
 #pragma unroll
-    for (int s = 0; s < k3Chunks; ++s) {
-        unsigned ua[8], ub[8];
+    for (int j = 0; j < k3Ops; ++j) {
+        unsigned ua[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int tap = k3_tap(kk, 2 * s + (e >> 2)), ch = e & 3;
-            // channel 3 of tap 0 carries the bias (every record's fourth channel is 1)
-            const float v = tap >= 27 ? 0.f : ch < 3 ? wl[co * 81 + ch * 27 + tap] : tap == 0 ? bias3[co] : 0.f;
+            const int q = 8 * j + e, u = q % 12;
+            const int tap = k3_tap(kk, q / 12), ch = u % 3, xp = u / 3;
+            const float v = tap >= 27 ? 0.f : wl[co * 81 + ch * 27 + tap];
             unsigned h, mm, lo;
             split3(v, h, mm, lo);
-            ua[e] = part ? mm : h;
-            ub[e] = part ? 0u : lo;
+            ua[e] = part ? (xp < 3 ? mm : 0u) : (xp < 3 ? h : lo);
         }
-        pa[s] = __builtin_bit_cast(bf8, mu4{ua[0] | (ua[1] << 16), ua[2] | (ua[3] << 16),
+        pa[j] = __builtin_bit_cast(bf8, mu4{ua[0] | (ua[1] << 16), ua[2] | (ua[3] << 16),
                                             ua[4] | (ua[5] << 16), ua[6] | (ua[7] << 16)});
-        pb[s] = __builtin_bit_cast(bf8, mu4{ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16),
-                                            ub[4] | (ub[5] << 16), ub[6] | (ub[7] << 16)});
+    }
+    mf16 bias16 = {};  // accumulator start: the bias in the upper rows
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        bias16[r] = bias3[4 * kk + r];
+        bias16[4 + r] = bias3[8 + 4 * kk + r];
     }
     __syncthreads();  // the W area becomes the first window
     if (begin < end) {
@@ -1555,9 +1569,9 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 // take as kw 1, 2 through the lane shift
                 bp[mt] = ((ti < 30 ? ti : 29) * 32 + m) * 4;
             }
-            mf16 acc[2] = {};
-            // the three splits of a tap row at kw 0 (one LDS read each), and at kw + 1 by the
-            // lane shift
+            mf16 acc[2] = {bias16, bias16};
+            // the three areas of a tap row's records at kw 0 (one LDS read each), and at kw + 1
+            // by the lane shift
             typedef mu2 Tap[3];
             auto rd = [&](int mt, int i, Tap& k) {
 #pragma unroll
@@ -1568,15 +1582,14 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
                 for (int sp = 0; sp < 3; ++sp) b[sp] = mu2{k3_next_lane(a[sp].x), k3_next_lane(a[sp].y)};
             };
-            // chunk s from its two taps: the four products, smallest first
+            // taps 2s, 2s + 1 of the half's sequence: 24 elements, three instructions
             auto chunk = [&](int s, int mt, const Tap& ta, const Tap& tb) {
-                const bf8 bh = __builtin_bit_cast(bf8, mu4{ta[0].x, ta[0].y, tb[0].x, tb[0].y});
-                const bf8 bm = __builtin_bit_cast(bf8, mu4{ta[1].x, ta[1].y, tb[1].x, tb[1].y});
-                const bf8 bl = __builtin_bit_cast(bf8, mu4{ta[2].x, ta[2].y, tb[2].x, tb[2].y});
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bl, acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bm, acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s], bh, acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], bh, acc[mt], 0, 0, 0);
+                const bf8 b0 = __builtin_bit_cast(bf8, mu4{ta[0].x, ta[0].y, ta[1].x, ta[1].y});
+                const bf8 b1 = __builtin_bit_cast(bf8, mu4{ta[2].x, ta[2].y, tb[0].x, tb[0].y});
+                const bf8 b2 = __builtin_bit_cast(bf8, mu4{tb[1].x, tb[1].y, tb[2].x, tb[2].y});
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[3 * s], b0, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[3 * s + 1], b1, acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[3 * s + 2], b2, acc[mt], 0, 0, 0);
             };
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {  // rows 2pr, 2pr + 1 of each half: chunks 3pr .. 3pr + 2
