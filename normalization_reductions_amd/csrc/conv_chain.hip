@@ -1427,22 +1427,38 @@ void conv3d_c3_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     // (rows 16..31) -- for K elements 8j .. 8j + 7 of its half: element q is element q % 12 of
     // tap k3_tap(kk, q / 12), channel q % 3 of x part (q % 12) / 3 (h, m, l, h), weighted
     // (Wh, Wh, Wh, Wl) in part 0 and (Wm, Wm, Wm, 0) in part 1
+    // (each of the lane's 42 weights is read and split once, two at a time by the packed
+    // conversion, and fills its 4 elements)
     const int co = m & 15, part = m >> 4;
     bf8 pa[k3Ops];
+    {
+        unsigned ua[k3Ops * 8];
+        auto place = [&](int slot, int ch, unsigned h, unsigned mm, unsigned lo) {
+            const int q = 12 * slot + ch;  // x parts h, m, l at q, q + 3, q + 6; h again at q + 9
+            ua[q] = ua[q + 3] = ua[q + 6] = (part ? mm : h) & 0xFFFFu;
+            ua[q + 9] = part ? 0u : lo & 0xFFFFu;
+        };
+        auto wt = [&](int slot, int ch) {
+            const int tap = k3_tap(kk, slot);
+            return tap >= 27 ? 0.f : wl[co * 81 + ch * 27 + tap];
+        };
 #pragma unroll
-    for (int j = 0; j < k3Ops; ++j) {
-        unsigned ua[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int q = 8 * j + e, u = q % 12;
-            const int tap = k3_tap(kk, q / 12), ch = u % 3, xp = u / 3;
-            const float v = tap >= 27 ? 0.f : wl[co * 81 + ch * 27 + tap];
+        for (int slot = 0; slot < 14; slot += 2) {
             unsigned h, mm, lo;
-            split3(v, h, mm, lo);
-            ua[e] = part ? (xp < 3 ? mm : 0u) : (xp < 3 ? h : lo);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                split3x2(wt(slot + d, 0), wt(slot + d, 1), h, mm, lo);
+                place(slot + d, 0, h, mm, lo);
+                place(slot + d, 1, h >> 16, mm >> 16, lo >> 16);
+            }
+            split3x2(wt(slot, 2), wt(slot + 1, 2), h, mm, lo);
+            place(slot, 2, h, mm, lo);
+            place(slot + 1, 2, h >> 16, mm >> 16, lo >> 16);
         }
-        pa[j] = __builtin_bit_cast(bf8, mu4{ua[0] | (ua[1] << 16), ua[2] | (ua[3] << 16),
-                                            ua[4] | (ua[5] << 16), ua[6] | (ua[7] << 16)});
+#pragma unroll
+        for (int j = 0; j < k3Ops; ++j)
+            pa[j] = __builtin_bit_cast(bf8, mu4{ua[8 * j] | (ua[8 * j + 1] << 16), ua[8 * j + 2] | (ua[8 * j + 3] << 16),
+                                                ua[8 * j + 4] | (ua[8 * j + 5] << 16), ua[8 * j + 6] | (ua[8 * j + 7] << 16)});
     }
     mf16 bias16 = {};  // accumulator start: the bias in the upper rows
 #pragma unroll
