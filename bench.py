@@ -469,8 +469,9 @@ def extras(torch, nra, x, y, steps, warmup):
 def conv_producers(steps, warmup):
     """The conv producers alone on the two model shapes (the eval entry point with running mean
     0, running variance 1, eps 0: W and b pass unchanged), each producer selected by the
-    library's NORMRED_CONV override: the vector-ALU direct kernel against the matrix-core
-    ones. Prints one JSON line of median ms per call (HIP events, a 512 MB read before each)."""
+    library's NORMRED_CONV override: the vector-ALU direct kernel, the fp32 matrix-instruction
+    producers and the default bf16-split ones. Prints one JSON line of median ms per call (HIP
+    events, a 512 MB read before each)."""
     import numpy as np
     import torch
 
@@ -490,7 +491,7 @@ def conv_producers(steps, warmup):
         out = torch.empty(oshape, device=dev)
         f = lambda: nra.conv_bn_eval_forward(*a, rm, rv, out=out, eps=0.0)
         times = {}
-        for mode in (["valu", "fp32", "default"] if wl == 4 else ["valu", "default"]):
+        for mode in ("valu", "fp32", "default"):
             if mode == "default":
                 os.environ.pop("NORMRED_CONV", None)
             else:
