@@ -969,6 +969,13 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     // in order, so the W staging waits for W alone while the window's loads are in flight
     constexpr int WPT = kC8Cout * kC8K / 256;
     static_assert(kC8Cout * kC8K % 256 == 0, "W values split evenly over the threads");
+    // eval mode: the fold's per-channel parameters go out first, so the fold waits for them
+    // alone (the loads complete in order)
+    float f_rv = 1.f, f_gm = 1.f;
+    if (MODE == kC8Conv && e.fold_rv && threadIdx.x < kC8Cout) {
+        f_rv = e.fold_rv[threadIdx.x];
+        if (e.gamma) f_gm = e.gamma[threadIdx.x];
+    }
     float wv[WPT];
 #pragma unroll
     for (int k = 0; k < WPT; ++k) wv[k] = w[(int)threadIdx.x + 256 * k];
@@ -988,12 +995,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         // eval mode folded in, with the fold kernel's arithmetic: each channel's factor once per
         // workgroup, while the W loads are in flight
         __shared__ float fold_a[kC8Cout];
-        if (threadIdx.x < kC8Cout) {
-            const int k = threadIdx.x;
-            const float inv = 1.0f / sqrtf(e.fold_rv[k] + e.eps);
-            const float gm = e.gamma ? e.gamma[k] : 1.f;
-            fold_a[k] = gm * inv * e.out_scale;
-        }
+        if (threadIdx.x < kC8Cout) fold_a[threadIdx.x] = f_gm * (1.0f / sqrtf(f_rv + e.eps)) * e.out_scale;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < WPT; ++k) wv[k] = wv[k] * fold_a[((int)threadIdx.x + 256 * k) / kC8K];
