@@ -908,7 +908,9 @@ __device__ __forceinline__ void c8_merge_publish(const C8Chain& e, int ch, Stat*
 // channel of (near) zero variance, where any difference between the two passes' values is
 // multiplied by 1/sqrt(eps): a constant input must give exactly beta * out_scale (BN page,
 // opening training-mode analysis).
-enum { kC8Conv = 0, kC8Stats = 1, kC8Apply = 2 };
+// kC8ApplyPlain is kC8Apply for chains without a pre-multiplier, clamp or post-multiplier (the
+// batch-norm model's): it skips the multiplications by 1, which leave every value as it is.
+enum { kC8Conv = 0, kC8Stats = 1, kC8Apply = 2, kC8ApplyPlain = 3 };
 
 template <int B, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -961,7 +963,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     if (MODE == kC8Stats && blockIdx.x == 0)
         for (int i = (int)threadIdx.x; i < 2 * kC8Cout; i += 256)
             __hip_atomic_store(e.xstats + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (MODE == kC8Apply)
+    constexpr bool APPLY = MODE == kC8Apply || MODE == kC8ApplyPlain;
+    if (APPLY)
         for (int ch = (int)blockIdx.x; ch < kC8Cout; ch += (int)gridDim.x)
             c8_merge_publish(e, ch, reinterpret_cast<Stat*>(win));
 
@@ -1038,7 +1041,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         pm0 = e.pre_mul[m];
         pm1 = e.pre_mul[32 + m];
     }
-    if (MODE == kC8Apply) {
+    if (APPLY) {
         A0 = (e.gamma ? e.gamma[m] : 1.f) * e.out_scale;  // times rstd once it is published
         A1 = (e.gamma ? e.gamma[32 + m] : 1.f) * e.out_scale;
         B0 = (e.beta ? e.beta[m] : 0.f) * e.out_scale;
@@ -1051,7 +1054,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     // The channel statistics, read before the first epilogue (after the first tile's matrix
     // work, which hides the merge): a bounded wait for the four tagged words of channels m and
     // 32 + m; if it gives up it raises the sticky flag (the results are then invalid).
-    bool have_stats = MODE != kC8Apply;
+    bool have_stats = !APPLY;
     auto fetch_stats = [&]() {
         unsigned long long w0, w1, w2, w3;
         uint32_t spins = 0;
@@ -1207,7 +1210,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         mf4 z = mf4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]} + bias;
-                        if (MODE == kC8Apply) {
+                        if (MODE == kC8ApplyPlain) {
+                            z = (z - mu) * A + Bc;
+                        } else if (MODE == kC8Apply) {
                             z = (mul_rn(z, pm) - mu) * A + Bc;
                             if (e.clamp) {
 #pragma unroll
@@ -2090,7 +2095,10 @@ hipError_t launch_conv2d_c8_bn_chain(const ConvGeom& g, const float* x, const fl
     conv2d_c8_bf16x6_kernel<kC8B, kC8Stats><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, nullptr, e);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    if (!e.pre_mul && !e.clamp && !e.post_mul)
+        conv2d_c8_bf16x6_kernel<kC8B, kC8ApplyPlain><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
+    else
+        conv2d_c8_bf16x6_kernel<kC8B, kC8Apply><<<dim3((unsigned)G), dim3(256), 0, stream>>>(g, x, w, b, out, e);
     return hipGetLastError();
 }
 
