@@ -872,7 +872,7 @@ constexpr uint32_t kC8Tag = 1u;  // the tag of a published word (cleared words c
 // tagged words and blends the batch statistics into the running ones (BN page, opening
 // analysis: running = (1 - m) * running + m * batch, with the unbiased batch variance). Every
 // thread of the workgroup calls it; red holds 4 Stats of scratch.
-__device__ __forceinline__ void c8_merge_publish(const C8Chain& e, int ch, Stat* red)
+__device__ __forceinline__ void c8_merge_publish(const C8Chain& e, const float* __restrict__ b, int ch, Stat* red)
 {
     const float4* pp = e.part + (int64_t)ch * e.nparts;
     Stat st = lane_strided_merge<256>(e.nparts, [&](int64_t i) {
@@ -889,8 +889,11 @@ __device__ __forceinline__ void c8_merge_publish(const C8Chain& e, int ch, Stat*
         xchg_store(e.xstats + 2 * ch, kC8Tag, t.mean);
         xchg_store(e.xstats + 2 * ch + 1, kC8Tag, rstd);
         if (e.run.mean) {
+            // the statistics leave the bias out (see the statistics pass); the batch mean of
+            // pre_mul * (conv + b) adds it back
             const float mo = e.run.momentum;
-            e.run.mean[ch] = (1.f - mo) * e.run.mean[ch] + mo * t.mean;
+            const float bm = b ? mul_rn(b[ch], e.pre_mul ? e.pre_mul[ch] : 1.f) : 0.f;
+            e.run.mean[ch] = (1.f - mo) * e.run.mean[ch] + mo * (t.mean + bm);
             e.run.var[ch] = (1.f - mo) * e.run.var[ch] + mo * (t.m2 / (t.n - 1.f));
         }
     }
@@ -898,10 +901,15 @@ __device__ __forceinline__ void c8_merge_publish(const C8Chain& e, int ch, Stat*
 }
 
 // Three modes share the producer: kC8Conv stores the conv output; kC8Stats stores nothing and
-// writes each workgroup's per-channel (count, mean, M2) of the values (conv + bias) * pre_mul,
-// for batch-norm statistics; kC8Apply recomputes the conv and stores the normalized chain
-// output ((v - mean) * rstd * gamma + beta) * out_scale, clamped, times post_mul, in the order
-// the chain epilogue uses.
+// writes each workgroup's per-channel (count, mean, M2) of the values conv * pre_mul, for
+// batch-norm statistics; kC8Apply recomputes the conv and stores the normalized chain output
+// ((v - mean) * rstd * gamma + beta) * out_scale, clamped, times post_mul, in the order the
+// chain epilogue uses, with v = conv * pre_mul.
+//
+// The bias is left out of both: batch norm subtracts each channel's mean, so pre_mul * (conv +
+// b) - mean(pre_mul * (conv + b)) is pre_mul * conv - mean(pre_mul * conv), and the apply pass
+// saves an add per value (and the two roundings it brings). The running mean, which is not
+// shift-invariant, adds pre_mul * b back.
 //
 // The statistics pass forms the same six products, in the same order, as the apply pass, so
 // its statistics are those of the very values the apply pass normalizes. That matters on a
@@ -966,7 +974,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     constexpr bool APPLY = MODE == kC8Apply || MODE == kC8ApplyPlain;
     if (APPLY)
         for (int ch = (int)blockIdx.x; ch < kC8Cout; ch += (int)gridDim.x)
-            c8_merge_publish(e, ch, reinterpret_cast<Stat*>(win));
+            c8_merge_publish(e, b, ch, reinterpret_cast<Stat*>(win));
 
     // all of a thread's W loads are issued at once, then the first window's: the loads complete
     // in order, so the W staging waits for W alone while the window's loads are in flight
@@ -1158,9 +1166,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 // positions ts + 8 (r / 4) + 4 kk + r % 4, increasing with r, so it owns the
                 // registers from r0 on. Each lane sums the raw conv sums shifted by its pivot
                 // (its first value of a tile with owned values, so a constant channel sums exact
-                // zeros and keeps the pivot as its mean): per tile, then into the lane's totals. The bias and
-                // pre-multiplier enter once per workgroup (mean (m + b) * pm, M2 * pm^2) when the
-                // partial is written, rounded as the apply pass rounds each value.
+                // zeros and keeps the pivot as its mean): per tile, then into the lane's totals. The
+                // pre-multiplier enters once per workgroup (mean m * pm, M2 * pm^2) when the partial is
+                // written, rounded as the apply pass rounds each value.
                 const int t = wave + 4 * i;
                 const int own = t < tiles ? 32 * t : BP;
                 if (cnt == 0.f) {  // nothing summed yet: (re)take the pivot
@@ -1209,7 +1217,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                     const float A = h ? A1 : A0, Bc = h ? B1 : B0, qm = h ? q1 : q0;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        mf4 z = mf4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]} + bias;
+                        mf4 z = mf4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+                        if (MODE == kC8Conv) z += bias;  // batch norm: the bias cancels (see above)
                         if (MODE == kC8ApplyPlain) {
                             z = (z - mu) * A + Bc;
                         } else if (MODE == kC8Apply) {
@@ -1266,8 +1275,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             Stat t = red[ch];
 #pragma unroll
             for (int v = 1; v < 4; ++v) t = chan_merge(t, red[v * kC8Cout + ch]);
-            const float bc = b ? b[ch] : 0.f, pc = e.pre_mul ? e.pre_mul[ch] : 1.f;
-            e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, mul_rn(t.mean + bc, pc), t.m2 * pc * pc, 0.f};
+            const float pc = e.pre_mul ? e.pre_mul[ch] : 1.f;
+            e.part[(int64_t)ch * gridDim.x + blockIdx.x] = float4{t.n, mul_rn(t.mean, pc), t.m2 * pc * pc, 0.f};
         }
     }
 }
