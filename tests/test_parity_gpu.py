@@ -1256,9 +1256,9 @@ def test_graph_capture_and_replay(dev, nra, orc):
     # pipelined), batch norm, the IN3d conv chain (4 items: statistics from a pass over the
     # conv output; 32 items, planar and channels last: statistics taken by the producer) and
     # the 2-D 64-wide producer's two chains (batch norm by recomputation, whose statistics pass
-    # clears the tagged words the apply pass publishes; eval mode folded into W) once, then
-    # replay three times with eager changes of the inputs in between, checking every replay
-    # against the oracle.
+    # clears the tagged words the apply pass publishes; eval mode folded into W) and the 3-D
+    # producer's eval conv once, then replay three times with eager changes of the inputs in
+    # between, checking every replay against the oracle.
     import torch
 
     g = np.random.Generator(np.random.PCG64(5150))
@@ -1278,8 +1278,11 @@ def test_graph_capture_and_replay(dev, nra, orc):
     rme = T(g.uniform(-0.5, 0.5, 64).astype(np.float32), dev)
     rve = T(g.uniform(0.5, 2.0, 64).astype(np.float32), dev)
     ye, yev = torch.empty((12, 64, 62, 62), device=dev), torch.empty((12, 64, 62, 62), device=dev)
+    rm3 = T(g.uniform(-0.3, 0.3, 16).astype(np.float32), dev)
+    rv3 = T(g.uniform(0.5, 2.0, 16).astype(np.float32), dev)
+    y3 = torch.empty((32, 16, 14, 30, 30), device=dev)
     s = torch.cuda.Stream(device=dev)
-    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(7)]
+    ws = [torch.zeros(1 << 26, dtype=torch.uint8, device=dev) for _ in range(8)]
     chain = dict(norm=nra.NR_NORM_INSTANCE, pre_mul=mc, clamp=(-1.0, 1.0), post_mul=mc,
                  reduce_max_c=True)
 
@@ -1294,6 +1297,7 @@ def test_graph_capture_and_replay(dev, nra, orc):
                                        beta=bte, out_scale=2.0, workspace=ws[5], stream=s)
         nra.conv_bn_eval_forward(xe, we, be, rme, rve, yev, gamma=ge, beta=bte, out_scale=2.0,
                                  workspace=ws[6], stream=s)
+        nra.conv_bn_eval_forward(xd, wc, bc, rm3, rv3, y3, out_scale=0.5, workspace=ws[7], stream=s)
 
     s.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(s):
@@ -1328,9 +1332,10 @@ def test_graph_capture_and_replay(dev, nra, orc):
                                                   gamma=i4["gamma"], beta=i4["beta"], out_scale=2.0))
         e7 = maxerr(H(yev), orc.conv_bn_eval(H(xe), i4["w"], i4["b"], H(rme), H(rve),
                                              gamma=i4["gamma"], beta=i4["beta"], scale=2.0))
-        _log("graph replay %d: max_abs_err %.3e %.3e %.3e %.3e %.3e %.3e %.3e"
-             % (rep, e1, e2, e3, e4, e5, e6, e7))
-        assert max(e1, e2, e3, e4, e5, e6, e7) <= TOL
+        e8 = maxerr(H(y3), orc.conv_bn_eval(H(xd), i5["w"], i5["b"], H(rm3), H(rv3), scale=0.5))
+        _log("graph replay %d: max_abs_err %.3e %.3e %.3e %.3e %.3e %.3e %.3e %.3e"
+             % (rep, e1, e2, e3, e4, e5, e6, e7, e8))
+        assert max(e1, e2, e3, e4, e5, e6, e7, e8) <= TOL
 
 
 def test_concurrent_streams(dev, nra, orc):
