@@ -1309,20 +1309,19 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 // slice: 4 rounds of 8 either way), and their reads are free of LDS bank conflicts: 32
 // consecutive positions cross a row, and the two lanes past the row's end hit the banks of the
 // row's first two records. The window of output slice o -- input slices o, o+1, o+2 -- sits in
-// LDS as the three bf16 splits of channels-last records: a ring of three 24 KB slots, so two
-// workgroups share a CU. The next input slice is loaded into registers during a step and split
-// into slice o's slot once every wave is done with it.
+// LDS as those 24-byte records: a ring of three 24 KB slots, so two workgroups share a CU. The
+// next input slice is loaded into registers during a step, then split and packed into slice o's
+// slot once every wave is done with it.
 // ---------------------------------------------------------------------------------------------
 constexpr int k3Pos = 900, k3Tiles = 30;  // positions and row tiles per output depth slice
-// ushorts of one split of one staged input slice, padded by 16 bytes: splits 8208 bytes apart
-// are read with one instruction each, straight into the operand's registers (at 8192 the
-// compiler pairs two splits of a tap into one read and then shuffles registers); the padding
-// keeps the staging's 16-byte writes aligned
+// ushorts of one area (an 8-byte piece of every position's record) of a staged input slice,
+// padded by 16 bytes: areas 8208 bytes apart are read with one instruction each, straight into
+// the operand's registers (at 8192 the compiler pairs two areas of a tap into one read and then
+// shuffles registers); the padding keeps the staging's 16-byte writes aligned
 constexpr int k3SplitU = 1024 * 4 + 8;
 constexpr int k3SlotU = 3 * k3SplitU;
-constexpr int k3Chunks = 7;  // tap pairs per lane half
-constexpr int k3Ops = 21;    // matrix instructions per tile: 14 taps x 12 elements / 8
-constexpr int k3Wgs = 2;                   // workgroups per CU (the LDS holds two rings)
+constexpr int k3Ops = 21;  // matrix instructions per tile: 14 taps x 12 elements / 8
+constexpr int k3Wgs = 2;   // workgroups per CU (the LDS holds two rings)
 
 // Tap sequence of a lane half. A tap row is (kd, kh), R = 3 kd + kh, holding taps 3R + kw. Half
 // 0 takes rows 0..3 and half 1 rows 4..7, each as kw = 0, 1, 2, so the halves run the same kw
