@@ -1055,7 +1055,9 @@ def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
 # crossing batch items, a single output slice (D = 3), and the many statistics slots of small
 # batches; every plan on top of it: instance norm with and without the channel max, batch
 # norm, and the eval fold
-C3_CASES = [(1, 3), (2, 5), (3, 4), (5, 7), (16, 4), (8, 16)]
+C3_CASES = [(1, 3), (2, 5), (3, 4), (5, 7), (16, 4), (8, 16),
+            (64, 3),   # one output slice per item: ranges of 3-4 rows cross items at every turn
+            (40, 5)]   # ranges spanning a few items, each restaging its window
 
 
 @pytest.mark.parametrize("cl", [False, True])
