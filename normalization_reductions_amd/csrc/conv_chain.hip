@@ -822,15 +822,17 @@ __global__ __launch_bounds__(256) void conv2d_c8_mfma32_kernel(ConvGeom g,
 // product x*w is taken as hh + hm + mh + mm + hl + lh. The dropped terms (ml, lm, ll) and the
 // two remainders e are each at most 2^-24 |x w|, the size of one fp32 rounding, so the conv
 // keeps fp32 accuracy. One v_mfma_f32_32x32x16_bf16 forms 16384 products in about half the
-// time the fp32 32x32x2 instruction takes for 2048, so the six passes need 2.4x fewer matrix
-// cycles than fp32 (K = 72 padded to 80).
+// time the fp32 32x32x2 instruction takes for 2048, so the six products' 27 instructions per 32
+// channels (K = 72, below) need 2.7x fewer matrix cycles than fp32's 36.
 //
 // K order: a lane-half supplies one 3x3 tap with all 8 input channels, 8 bf16 that one 16-byte
 // LDS read fetches, so the staged window is channels-last: [split][row][column][channel].
-// Chunk q pairs tap 2q (lanes 0..31) with tap 2q + 1 (lanes 32..63); the tenth tap is padding
-// with zero weights whose lanes re-read tap 8, so the operand stays finite. A and B map
-// (lane-half, element) to k the same way, so the products pair up in whatever order the
-// instruction sums them. D has the 32x32 layout of the fp32 kernel above.
+// Chunk q < 4 pairs tap 2q (lanes 0..31) with tap 2q + 1 (lanes 32..63), six instructions for
+// its six products. Tap 8 fills the last chunk on its own: both lane halves take it, each with
+// other parts ([xl | xm] x [wh | wm], [xm | xh] x [wh | wl], [xh | xh] x [wh | wm]), three
+// instructions for the same six products -- 27 per 32 channels instead of the 30 a zero padding
+// tap would take. A and B map (lane-half, element) to k the same way, so the products pair up
+// in whatever order the instruction sums them. D has the 32x32 layout of the fp32 kernel above.
 // ---------------------------------------------------------------------------------------------
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef unsigned int mu4 __attribute__((ext_vector_type(4)));
@@ -997,11 +999,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
     // out in LDS as [nt][q][split][lane] x 8 bf16, from where every lane takes its operands
     // with 16-byte reads (gathering them per lane touched a cache line per lane and load).
     // The window buffers hold them until the first window is staged.
+    // The last chunk holds tap 8 alone: both lane halves take it, each with other parts (see
+    // the matrix loop), so its two operands are [h | m] and [h | l] of tap 8 (slots 0 and 1).
     static_assert(4 * kC8Cout * sizeof(Stat) <= 2 * WIN * sizeof(unsigned short), "partials fit");
-    for (int i = (int)threadIdx.x; i < 2 * 3 * 32; i += 256) {  // the padding tap's operands
-        const int nt = i / 96, sp = (i / 32) % 3, lane = 32 + i % 32;
-        *reinterpret_cast<mu4*>(win + (((nt * kBfChunks + kBfChunks - 1) * 3 + sp) * 64 + lane) * 8) = mu4{0, 0, 0, 0};
-    }
     if (MODE == kC8Conv && e.fold_rv) {
         // eval mode folded in, with the fold kernel's arithmetic: each channel's factor once per
         // workgroup, while the W loads are in flight
@@ -1018,9 +1018,15 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         unsigned h, mm, lo;
         split3(wv[k], h, mm, lo);
         unsigned short* d = win + (((n >> 5) * kBfChunks + (tap >> 1)) * 3 * 64 + (n & 31) + 32 * (tap & 1)) * 8 + ci;
-        d[0] = (unsigned short)h;
-        d[64 * 8] = (unsigned short)mm;
-        d[2 * 64 * 8] = (unsigned short)lo;
+        if (tap < 8) {
+            d[0] = (unsigned short)h;
+            d[64 * 8] = (unsigned short)mm;
+            d[2 * 64 * 8] = (unsigned short)lo;
+        } else {
+            d[0] = d[64 * 8] = (unsigned short)h;      // lanes 0..31 of slots 0, 1: h
+            d[32 * 8] = (unsigned short)mm;            // lanes 32..63: m (slot 0), l (slot 1)
+            d[(64 + 32) * 8] = (unsigned short)lo;
+        }
     }
     __syncthreads();
     bf8 wb[2][kBfChunks][3];
@@ -1029,7 +1035,7 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
         for (int q = 0; q < kBfChunks; ++q)
 #pragma unroll
-            for (int sp = 0; sp < 3; ++sp)
+            for (int sp = 0; sp < (q < kBfChunks - 1 ? 3 : 2); ++sp)
                 wb[nt][q][sp] = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(win + (((nt * kBfChunks + q) * 3 + sp) * 64 + l) * 8));
     __syncthreads();
     float bias0 = b ? b[m] : 0.f, bias1 = b ? b[32 + m] : 0.f;
@@ -1141,9 +1147,9 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
             // instructions (-6 %); the storing passes do not
             if (MODE == kC8Stats) __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
-            for (int q = 0; q < kBfChunks; ++q) {
-                const int off = (q == 0 ? 0 : q == 1 ? 2 : q == 2 ? W + 1 : q == 3 ? 2 * W : 2 * W + 2) * kC8Cin;
-                const unsigned short* a = q == 1 ? a2 : q == 4 ? a0 : a1;
+            for (int q = 0; q < kBfChunks - 1; ++q) {
+                const int off = (q == 0 ? 0 : q == 1 ? 2 : q == 2 ? W + 1 : 2 * W) * kC8Cin;
+                const unsigned short* a = q == 1 ? a2 : a1;
                 const bf8 ah = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off));
                 const bf8 am = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + SPLIT));
                 const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + off + 2 * SPLIT));
@@ -1159,6 +1165,21 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, wb[1][q][0], acc1, 0, 0, 0);
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[0][q][0], acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wb[1][q][0], acc1, 0, 0, 0);
+            }
+            {
+                // tap 8 in both lane halves, three instructions for its six products (smallest
+                // first): [xl | xm] x [wh | wm] = lh, mm; [xm | xh] x [wh | wl] = mh, hl;
+                // [xh | xh] x [wh | wm] = hh, hm. Half 1 reads the next part down of half 0's.
+                const unsigned short* a = a0 + (2 * W + 2) * kC8Cin + (kk ? 0 : SPLIT);
+                const bf8 xh = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a0 + (2 * W + 2) * kC8Cin));
+                const bf8 xb = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a));
+                const bf8 xc = __builtin_bit_cast(bf8, *reinterpret_cast<const mu4*>(a + SPLIT));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xc, wb[0][kBfChunks - 1][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xc, wb[1][kBfChunks - 1][0], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, wb[0][kBfChunks - 1][1], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, wb[1][kBfChunks - 1][1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, wb[0][kBfChunks - 1][0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, wb[1][kBfChunks - 1][0], acc1, 0, 0, 0);
             }
             if (MODE == kC8Stats) {
                 // positions this tile owns: from 32 t on for a tile t < tiles (an overlapping
