@@ -1125,7 +1125,13 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
         const int o0 = (int)(box - n * nbox) * B;
         const int BP = min(B, OH - o0) * OW;  // positions in this box: a multiple of 4, >= 62
         // lane l stores 16 bytes of channel l / 8 + 8 s at position 4 (l % 8) of a tile
-        float* cb = MODE == kC8Stats ? nullptr : c + (n * kC8Cout + (l >> 3)) * g.SP + (int64_t)o0 * OW + 4 * (l & 7);
+        // stores through a buffer resource over batch item n's output (64 SP floats, below 2^31
+        // bytes): the lane's byte offset in a register, channel block (32 h + 8 s)'s in a scalar
+        // register, so no store needs its own 64-bit address arithmetic
+        const __amdgpu_buffer_rsrc_t cres = __builtin_amdgcn_make_buffer_rsrc(
+            MODE == kC8Stats ? (float*)nullptr : c + n * kC8Cout * g.SP, 0, (int)(kC8Cout * g.SP * 4),
+            0x00020000 /* 32-bit data format */);
+        const int lane_off = (int)(((l >> 3) * g.SP + o0 * OW + 4 * (l & 7)) * 4);
         // exactly TPW tiles per wave, each 32 whole positions of the box: the last tile ends at
         // the box's last position (overlapping the one before), and waves with no tile left
         // repeat the last. Overlaps rewrite bitwise-identical values, and every lane issues the
@@ -1256,7 +1262,8 @@ void conv2d_c8_bf16x6_kernel(ConvGeom g, const float* __restrict__ x, const floa
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const mf4 z = *reinterpret_cast<const mf4*>(trw + ((l >> 3) + 8 * s) * TR + 4 * (l & 7));
-                        *reinterpret_cast<mf4*>(cb + (int64_t)(32 * h + 8 * s) * g.SP + ts) = z;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(mu4, z), cres, lane_off + 4 * ts,
+                                                               (int)((32 * h + 8 * s) * g.SP * 4), 0);
                     }
                     __builtin_amdgcn_wave_barrier();
                 }
@@ -2090,7 +2097,7 @@ hipError_t launch_conv3d_c3(const ConvGeom& g, const float* x, const float* w, c
 bool conv2d_c8_shape(const ConvGeom& g)
 {
     return !g.cl && g.dims == 2 && g.Cin == kC8Cin && g.Cout == kC8Cout && g.W == kC8W &&
-           g.SP % 4 == 0 && g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP < (1LL << 31);
+           g.SP % 4 == 0 && g.Cin * g.D * g.H * g.W < (1LL << 31) && g.SP * kC8Cout * 4 < (1LL << 31);
 }
 
 int64_t conv2d_c8_stats_grid(const ConvGeom& g) { return c8_grid(g); }
