@@ -610,7 +610,9 @@ def test_conv_bn_workload4_full(dev, nra, orc):
     args = (t(inp["x"]), t(inp["w"]), t(inp["b"]))
     kw = dict(norm=nra.NR_NORM_BATCH_TRAIN, eps=inp["eps"], gamma=t(inp["gamma"]),
               beta=t(inp["beta"]), out_scale=inp["scale"])
-    out = nra.conv_norm_epilogue_forward(*args, **kw)
+    # the output starts as NaN, so a position left unwritten fails the comparison
+    out = torch.full((128, 64, 62, 62), float("nan"), device=dev)
+    nra.conv_norm_epilogue_forward(*args, out, **kw)
     ref = orc.conv_norm_epilogue(inp["x"], inp["w"], inp["b"], batch=True, gamma=inp["gamma"],
                                  beta=inp["beta"], out_scale=inp["scale"])
     err = maxerr(H(out), ref)
@@ -1034,7 +1036,12 @@ def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
     rm0 = g.uniform(-0.2, 0.2, 64).astype(np.float32)
     rv0 = g.uniform(0.5, 1.5, 64).astype(np.float32)
     rm, rv = T(rm0, dev), T(rv0, dev)
-    out = nra.conv_norm_epilogue_forward(T(x, dev), T(w, dev), T(b, dev), norm=nra.NR_NORM_BATCH_TRAIN,
+    import torch
+
+    # outputs start as NaN: every position must be written (the producer drops the stores of
+    # positions an earlier tile of the same box wrote)
+    nan_out = lambda: torch.full((n, 64, h - 2, 62), float("nan"), device=dev)
+    out = nra.conv_norm_epilogue_forward(T(x, dev), T(w, dev), T(b, dev), nan_out(), norm=nra.NR_NORM_BATCH_TRAIN,
                                          gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0,
                                          running_mean=rm, running_var=rv, momentum=0.3)
     err = maxerr(H(out), orc.conv_norm_epilogue(x, w, b, batch=True, gamma=gm, beta=bt, out_scale=2.0))
@@ -1042,7 +1049,7 @@ def test_conv2d_64wide_box_geometry(dev, nra, orc, n, h):
     _, mean, var = orc.batch_norm_train(c, with_stats=True)
     rm_ref, rv_ref = orc.bn_running_update(mean, var, c.size // 64, rm0, rv0, momentum=0.3)
     _check_running(rm, rv, rm_ref, rv_ref, "conv2d 64-wide n %d h %d" % (n, h))
-    ev = nra.conv_bn_eval_forward(T(x, dev), T(w, dev), T(b, dev), T(rm0, dev), T(rv0, dev),
+    ev = nra.conv_bn_eval_forward(T(x, dev), T(w, dev), T(b, dev), T(rm0, dev), T(rv0, dev), nan_out(),
                                   gamma=T(gm, dev), beta=T(bt, dev), out_scale=2.0)
     err_ev = maxerr(H(ev), orc.conv_bn_eval(x, w, b, rm0, rv0, gamma=gm, beta=bt, scale=2.0))
     _log("conv2d 64-wide n %d h %d: bn max_abs_err %.3e, eval %.3e" % (n, h, err, err_ev))
